@@ -1,0 +1,271 @@
+"""Benchmark of the bf16 routed MoE-LoRA layer on one MI355X.
+
+One step = one full layer forward from router logits (routing, permutation,
+both LoRA shrinks, gate_up GEMM with LoRA expand and SwiGLU, down GEMM with
+LoRA expand, finalize) over one batch of seeded synthetic inputs already
+resident in HBM.  Prints ONE JSON line on stdout; diagnostics go to stderr.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode64]
+
+Per-kernel durations come from HIP events recorded by the library at its
+stage boundaries on the launch stream during the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-LoRA layer tokens/s + achieved HBM GB/s (T=64 decode) and MFMA % (prefill)"
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+WORKLOAD_TEXT = {
+    "decode64": "multi-adapter decode: T=64 tokens, hidden 2048, 128 experts top-8, inter 768 "
+                "SwiGLU, 4 LoRA adapters rank 16 on gate_up and down, mapping uniform over "
+                "{-1,0,1,2,3}, 4 hot experts",
+    "decode16": "decode: T=16, hidden 2048, 128 experts top-8, inter 768, 1 adapter rank 16",
+    "ep_shard": "expert-parallel shard: T=64, hidden 2048, 32 of 128 experts local (offset 32), "
+                "top-8, inter 768, 4 adapters rank 16",
+    "prefill": "prefill: T=2048, hidden 2048, 128 experts top-8, inter 768, 4 adapters rank 64 "
+               "in runs of 512 tokens",
+    "tiny": "tiny: T=8, hidden 128, 8 experts top-2, inter 64, 2 adapters rank 4",
+}
+
+
+def log(msg: str):
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+class HipEvents:
+    """Minimal HIP event API through ctypes (timing on the library's stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n: int):
+        out = []
+        for _ in range(n):
+            ev = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(ev))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            out.append(ev.value)
+        return out
+
+    def record(self, ev, stream):
+        rc = self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def sync(self, ev):
+        self.hip.hipEventSynchronize(ctypes.c_void_p(ev))
+
+    def destroy(self, evs):
+        for ev in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def algorithmic_cost(cfg, ids, mapping):
+    """Bytes the layer must move and flops it must do, from the actual routing.
+
+    Expert weights of every touched local expert, LoRA stacks of every touched
+    (adapter, local expert) pair, plus hidden in, out, logits and mapping.
+    Also the bytes of the gate_up GEMM launch alone.
+    """
+    import numpy as np
+    T, H, I, E, k = cfg.num_tokens, cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k
+    off, E_l, L = cfg.local_expert_offset, cfg.local_num_experts, cfg.num_loras
+    rg, rd = cfg.rank_gate_up, cfg.rank_down
+    ids = np.asarray(ids)
+    local = (ids >= off) & (ids < off + E_l)
+    le = np.where(local, ids - off, -1)
+    touched = np.unique(le[local])
+    lmap = np.repeat(np.asarray(mapping), k).reshape(ids.shape)
+    lvalid = local & (lmap >= 0) & (lmap < L)
+    pairs = np.unique((lmap * E_l + le)[lvalid]) if L > 0 else np.zeros(0)
+    P = int(local.sum())
+    P_lora = int(lvalid.sum())
+    n_e, n_pairs = len(touched), len(pairs)
+    w13_bytes = 2 * n_e * H * 2 * I
+    w2_bytes = 2 * n_e * I * H
+    lora_gu = 2 * n_pairs * (rg * H + 2 * I * rg) if rg else 0
+    lora_dn = 2 * n_pairs * (rd * I + H * rd) if rd else 0
+    io = 2 * T * H * 2 + 4 * T * E + 4 * T
+    total_bytes = w13_bytes + w2_bytes + lora_gu + lora_dn + io
+    flops = 2 * P * (H * 2 * I + I * H) + 2 * P_lora * (rg * (H + 2 * I) + rd * (I + H))
+    # gate_up GEMM launch: W13 of touched experts, B_gu of touched pairs, the routed
+    # tokens' hidden rows, the bf16 shrink rows it reads, the activation it writes
+    tok_touched = int(local.any(axis=1).sum())
+    gate_up_bytes = (w13_bytes + (2 * n_pairs * 2 * I * rg if rg else 0) + 2 * tok_touched * H +
+                     2 * P_lora * ((rg + 7) // 8 * 8) + 2 * P * I)
+    gate_up_flops = 2 * P * H * 2 * I + 2 * P_lora * rg * 2 * I
+    return {
+        "bytes": int(total_bytes), "flops": int(flops), "local_slots": P,
+        "touched_experts": n_e, "touched_lora_pairs": n_pairs,
+        "gate_up_bytes": int(gate_up_bytes), "gate_up_flops": int(gate_up_flops),
+    }
+
+
+def cpu_baseline(cfg, inp, min_seconds: float):
+    """Time the CPU oracle (as is) on a bounded sample of the same workload."""
+    import numpy as np
+    from oracle import oracle
+    T = cfg.num_tokens
+    n_tok = min(T, 64)
+    toks = np.linspace(0, T - 1, n_tok).astype(np.int32) if n_tok < T else None
+    ids, w = oracle.route(inp["logits"], cfg.top_k)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.forward(cfg, inp, topk_ids=ids, topk_weights=w, tokens=toks)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    sample = (f"{n_tok} of {T} tokens" + ("" if toks is None else " (evenly spaced)") +
+              f" of the same seeded batch, routing precomputed, {reps} repetitions, {el:.1f} s")
+    return {"value": reps * n_tok / el, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": sample}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode64", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU oracle baseline time budget (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this layer runs on one GPU; --gpus {args.gpus} is not supported "
+              "(multi-GPU expert parallelism is a design note only)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_up_amd import binding
+    from mixture_experts_layer_up_amd.synth import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.workload]
+    log(f"[bench] generating {args.workload} inputs")
+    inp = make_inputs(cfg)
+    torch.cuda.set_device(0)
+    shape, lay = binding.layer_from_host(cfg, inp)
+    ws = torch.empty(binding.workspace_size(shape), dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    kw = {k: v for k, v in lay.items() if k not in ("hidden", "w13_packed", "w2_packed")}
+
+    def step(events=None):
+        binding.forward(shape, lay["hidden"], lay["w13_packed"], lay["w2_packed"], out=out,
+                        workspace=ws, stage_events=events, **kw)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    hip = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    K = args.steps
+    evs = [hip.create(binding.NUM_STAGE_EVENTS) for _ in range(K)]
+    start, end = hip.create(2)
+    log(f"[bench] timing {K} steps")
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    hip.record(start, stream)
+    for s in range(K):
+        step(evs[s])
+    hip.record(end, stream)
+    hip.sync(end)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    total_ms = hip.elapsed_ms(start, end)
+    ms_per_step = total_ms / K
+    stage_ms = np.zeros(len(binding.STAGE_NAMES))
+    for s in range(K):
+        for i in range(len(binding.STAGE_NAMES)):
+            stage_ms[i] += hip.elapsed_ms(evs[s][i], evs[s][i + 1])
+    stage_ms /= K
+    for e in evs:
+        hip.destroy(e)
+    hip.destroy([start, end])
+
+    # the cost model counts what this batch's routing touches (the library's own routing)
+    routing = binding.alloc_routing(shape, "cuda")
+    binding.forward(shape, lay["hidden"], lay["w13_packed"], lay["w2_packed"], out=out,
+                    workspace=ws, routing=routing, **kw)
+    torch.cuda.synchronize()
+    cost = algorithmic_cost(cfg, routing["topk_ids"].cpu().numpy(), inp["mapping"])
+    t_s = ms_per_step / 1e3
+    gate_up_ms = float(stage_ms[binding.STAGE_NAMES.index("gemm_gate_up_swiglu")])
+    achieved = cost["gate_up_bytes"] / (gate_up_ms / 1e3) / 1e9
+    layer_gbps = cost["bytes"] / t_s / 1e9
+    layer_tflops = cost["flops"] / t_s / 1e12
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("[bench] CPU oracle baseline")
+        cpu = cpu_baseline(cfg, inp, args.cpu_seconds)
+
+    result = {
+        "metric": METRIC,
+        "value": cfg.num_tokens / t_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded numpy PCG64; random-init weights of the layer's shapes)",
+        "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}",
+                   "num_tokens": cfg.num_tokens, "hidden": cfg.hidden, "inter": cfg.inter,
+                   "num_experts": cfg.num_experts, "top_k": cfg.top_k,
+                   "local_expert_offset": cfg.local_expert_offset,
+                   "local_num_experts": cfg.local_num_experts, "num_loras": cfg.num_loras,
+                   "rank": cfg.rank_gate_up, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "gemm_gate_up_swiglu",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None},
+        "layer": {"algorithmic_bytes": cost["bytes"], "flops": cost["flops"],
+                  "hbm_gbps": layer_gbps, "hbm_frac": layer_gbps / HBM_PEAK_GBPS,
+                  "mfma_tflops": layer_tflops, "mfma_frac": layer_tflops / MFMA_BF16_PEAK_TFLOPS,
+                  "touched_experts": cost["touched_experts"],
+                  "touched_lora_pairs": cost["touched_lora_pairs"],
+                  "local_slots": cost["local_slots"]},
+        "stages_us": {n: float(v * 1e3) for n, v in zip(binding.STAGE_NAMES, stage_ms)},
+        "wall_ms_per_step": wall_s * 1e3 / K,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

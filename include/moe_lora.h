@@ -1,0 +1,210 @@
+/*
+ * moe_lora.h -- C ABI of the MI355X (gfx950) bf16 routed MoE-LoRA layer.
+ *
+ * One layer forward: top-k routing -> expert permutation -> gate_up grouped
+ * GEMM with the per-adapter LoRA delta added before SwiGLU -> down grouped
+ * GEMM with the down LoRA delta -> routing-weighted finalize back to tokens.
+ * Sources for the operation:
+ *   "BF16 support for the experimental_sgl_trtllm MoE-LoRA path" (GitHub PR
+ *   page), "Files changed" table (launcher row: the pipeline order, where the
+ *   gate_up delta enters, what the activation writes) and Flow sections 1
+ *   and 2 (which LoRA add is weighted by the routing weight, virtual-expert
+ *   addressing of the LoRA weights, expert-parallel masking);
+ *   "sglang PR #28953 digest", change summary (permuted index -1 for
+ *   expert-parallel slots that are not local; never written through).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless stated otherwise; the shape
+ *     structs are HOST memory read during the call only.
+ *   - bf16 tensors are passed as `const void*` holding IEEE bfloat16 bits,
+ *     row-major, contiguous.  16-byte alignment is required where noted.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All device
+ *     work is enqueued on it and the call returns without waiting; inputs
+ *     must stay valid until the stream has passed the call.
+ *   - The library never allocates device memory and never synchronises the
+ *     host inside moe_lora_route / moe_lora_forward, so both can be captured
+ *     into a HIP graph.  It keeps no state between calls; concurrent calls
+ *     are safe when they use distinct outputs and workspaces.
+ *   - Host-side validation needs no GPU: bad arguments return a negative
+ *     status before any HIP call.  No entry point throws.
+ *   - Device data that is out of range never faults: a top-k id outside
+ *     [local_expert_offset, local_expert_offset + local_num_experts) is a
+ *     non-local slot (contributes nothing), and a token_lora_mapping value
+ *     outside [-1, num_loras) is treated as -1 (no adapter).
+ */
+#ifndef MOE_LORA_H_
+#define MOE_LORA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MOE_LORA_OK                       0
+#define MOE_LORA_ERR_INVALID_ARG         -1 /* null pointer, bad combination */
+#define MOE_LORA_ERR_UNSUPPORTED_SHAPE   -2 /* dimension outside the limits below */
+#define MOE_LORA_ERR_WORKSPACE_TOO_SMALL -3
+#define MOE_LORA_ERR_MISALIGNED          -4 /* pointer not aligned as required */
+#define MOE_LORA_ERR_HIP                 -5 /* a HIP launch or event call failed */
+
+/* Number of events moe_lora_forward records when moe_lora_inputs.stage_events
+ * is set: before routing, then after each of routing+permute, gate_up LoRA
+ * shrink, gate_up GEMM (+SwiGLU), down LoRA shrink, down GEMM, finalize. */
+#define MOE_LORA_NUM_STAGE_EVENTS 7
+
+/*
+ * Layer shape.  Limits (else MOE_LORA_ERR_UNSUPPORTED_SHAPE):
+ *   0 <= num_tokens, num_tokens * top_k <= 2^24
+ *   hidden % 64 == 0, 64 <= hidden <= 65536
+ *   inter % 32 == 0, 32 <= inter <= 65536
+ *   1 <= num_experts <= 1024, 1 <= top_k <= min(64, num_experts)
+ *   0 <= local_expert_offset, 1 <= local_num_experts,
+ *   local_expert_offset + local_num_experts <= num_experts
+ *   0 <= num_loras <= 64, num_loras * local_num_experts <= 8192
+ *   0 <= rank_gate_up, rank_down <= 256
+ * A LoRA projection is active when num_loras > 0 and its rank > 0.
+ */
+typedef struct moe_lora_shape {
+    int32_t num_tokens;            /* T */
+    int32_t hidden;                /* H */
+    int32_t inter;                 /* I, per expert; gate_up width is 2I */
+    int32_t num_experts;           /* E: routed (global) experts */
+    int32_t top_k;                 /* k */
+    int32_t local_expert_offset;   /* first expert this shard owns */
+    int32_t local_num_experts;     /* E_l: experts this shard owns */
+    int32_t num_loras;             /* L: adapters in the stacks */
+    int32_t rank_gate_up;          /* r_gu */
+    int32_t rank_down;             /* r_dn */
+    float routed_scaling_factor;   /* multiplies the routed sum (1.0 = none) */
+} moe_lora_shape;
+
+/*
+ * Routing results (device arrays, caller-owned).  Slot x = t * top_k + j.
+ *   topk_ids      [T, k] int32  global expert ids, ordered by (logit desc,
+ *                               id asc)
+ *   topk_weights  [T, k] fp32   softmax over the k selected logits
+ *   expert_counts [E_l]         local slots per local expert
+ *   expert_offsets[E_l + 1]     exclusive prefix sum; [E_l] = P, the number
+ *                               of local slots
+ *   expanded_idx_to_permuted_idx [T*k]  permuted row p of slot x, or -1 for
+ *                               a non-local slot; rows are expert-contiguous
+ *                               and ascending in x inside one expert
+ *   permuted_idx_to_expanded_idx [T*k]  inverse; entries [P, T*k) are -1
+ *   lora_seg_offsets [L * E_l + 1]      exclusive prefix sum of the local
+ *                               slots whose token has an adapter, keyed by
+ *                               the virtual expert (adapter, local expert)
+ *   lora_seg_slots   [T*k]      those slots (x), grouped by key, ascending
+ *                               x inside a key; unused tail is -1
+ */
+typedef struct moe_lora_routing {
+    int32_t *topk_ids;
+    float *topk_weights;
+    int32_t *expert_counts;
+    int32_t *expert_offsets;
+    int32_t *expanded_idx_to_permuted_idx;
+    int32_t *permuted_idx_to_expanded_idx;
+    int32_t *lora_seg_offsets;
+    int32_t *lora_seg_slots;
+} moe_lora_routing;
+
+/*
+ * Forward inputs.  Exactly one of `router_logits` or the pair
+ * (`topk_ids`, `topk_weights`) is given.
+ *   hidden             bf16 [T, H], 16-byte aligned
+ *   router_logits      fp32 [T, E]
+ *   topk_ids           int32 [T, k] (any value; out-of-window ids are
+ *                      non-local slots), topk_weights fp32 [T, k]
+ *   w13_packed         expert gate_up weights [E_l, H, 2I] (columns [0, I)
+ *                      gate, [I, 2I) up) in the packed layout written by
+ *                      moe_lora_pack_weights; 16-byte aligned
+ *   w2_packed          expert down weights [E_l, I, H], packed; 16-byte aligned
+ *   lora_a_gate_up     bf16 [L, E_l, r_gu, H]   (shrink, 16-byte aligned)
+ *   lora_b_gate_up     bf16 [L, E_l, 2I, r_gu]  (expand; 16-byte aligned
+ *                      when r_gu % 8 == 0, else 2-byte)
+ *   lora_a_down        bf16 [L, E_l, r_dn, I]
+ *   lora_b_down        bf16 [L, E_l, H, r_dn]
+ *   token_lora_mapping int32 [T], adapter of each token, -1 = none; NULL
+ *                      means every token is -1
+ *   stage_events       NULL, or MOE_LORA_NUM_STAGE_EVENTS hipEvent_t handles
+ *                      recorded on `stream` at the stage boundaries (for
+ *                      per-kernel timing); stages that do not run still get
+ *                      their event recorded
+ * LoRA pointers may be NULL when the projection is inactive.
+ */
+typedef struct moe_lora_inputs {
+    const void *hidden;
+    const float *router_logits;
+    const int32_t *topk_ids;
+    const float *topk_weights;
+    const void *w13_packed;
+    const void *w2_packed;
+    const void *lora_a_gate_up;
+    const void *lora_b_gate_up;
+    const void *lora_a_down;
+    const void *lora_b_down;
+    const int32_t *token_lora_mapping;
+    void *const *stage_events;
+} moe_lora_inputs;
+
+/* Bytes of device workspace moe_lora_forward needs for `shape` (host only,
+ * pure; 0 for an invalid shape).  The workspace must be 256-byte aligned. */
+size_t moe_lora_workspace_size(const moe_lora_shape *shape);
+
+/* Bytes of the packed expert weights (equal to the unpacked sizes). */
+size_t moe_lora_packed_w13_bytes(const moe_lora_shape *shape);
+size_t moe_lora_packed_w2_bytes(const moe_lora_shape *shape);
+
+/*
+ * One-time relayout of the expert weights into the MFMA operand layout the
+ * grouped GEMMs stream (the pages' path likewise prepares its expert weights
+ * once at load: "BF16 support for the experimental_sgl_trtllm MoE-LoRA path",
+ * Summary and "Files changed" table, base_backend row).
+ *   w13 bf16 [E_l, H, 2I] -> w13_packed, w2 bf16 [E_l, I, H] -> w2_packed.
+ * Packed layout: for expert e, column tile n (16 columns), K chunk c (32
+ * rows), lane l (0..63), element i (0..7), the bf16 at
+ *   ((e * NT + n) * KC + c) * 512 + l * 8 + i
+ * is W[e][32c + 8(l / 16) + i][col(n) + l % 16], with NT = N / 16, KC = K/32.
+ * For w13, col(n) = (n % 2) * I + (n / 2) * 16 (gate and up tiles of the same
+ * columns alternate); for w2, col(n) = 16 n.  All four pointers 16-byte
+ * aligned; outputs must not overlap inputs.
+ */
+int moe_lora_pack_weights(const moe_lora_shape *shape, const void *w13, const void *w2,
+                          void *w13_packed, void *w2_packed, void *stream);
+
+/*
+ * Routing and permutation only.  Routes from `router_logits` when given,
+ * else takes `topk_ids` / `topk_weights` as they are (then routing->topk_ids
+ * and routing->topk_weights are not written and may be NULL).  Every other
+ * field of `routing` must be non-NULL.  `token_lora_mapping` as in
+ * moe_lora_inputs.  Needs no workspace.
+ */
+int moe_lora_route(const moe_lora_shape *shape, const float *router_logits,
+                   const int32_t *topk_ids, const float *topk_weights,
+                   const int32_t *token_lora_mapping, const moe_lora_routing *routing,
+                   void *stream);
+
+/*
+ * The layer forward.  Writes `out` bf16 [T, H] (16-byte aligned) completely:
+ * rows of tokens with no local slot are 0, so `out` needs no clearing.  With
+ * several expert-parallel shards, `out` is this shard's partial sum.
+ * `routing` is NULL, or receives the routing arrays as moe_lora_route
+ * defines them (then all its fields are written except topk_ids /
+ * topk_weights when top-k was given).  `workspace` is device memory of at
+ * least moe_lora_workspace_size(shape) bytes, 256-byte aligned; its
+ * contents on entry do not matter.
+ */
+int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *inputs,
+                     const moe_lora_routing *routing, void *out, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *moe_lora_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LORA_H_ */

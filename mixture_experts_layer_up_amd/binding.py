@@ -1,0 +1,261 @@
+"""ctypes binding of ``libmoe_lora.so``: argument marshalling only.
+
+Every step of the layer runs in the HIP library; this module checks tensor
+shapes / dtypes / devices, takes raw device pointers from torch tensors and
+passes the current HIP stream.  torch is used for device memory and streams
+only.  If the library is not built, loading fails loudly; there is no other
+implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Dict, Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_lora.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe_lora.h")
+
+_lib = None
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("inter", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("local_expert_offset", ctypes.c_int32),
+        ("local_num_experts", ctypes.c_int32),
+        ("num_loras", ctypes.c_int32),
+        ("rank_gate_up", ctypes.c_int32),
+        ("rank_down", ctypes.c_int32),
+        ("routed_scaling_factor", ctypes.c_float),
+    ]
+
+
+class Routing(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "topk_ids", "topk_weights", "expert_counts", "expert_offsets",
+        "expanded_idx_to_permuted_idx", "permuted_idx_to_expanded_idx",
+        "lora_seg_offsets", "lora_seg_slots")]
+
+
+class Inputs(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "hidden", "router_logits", "topk_ids", "topk_weights", "w13_packed", "w2_packed",
+        "lora_a_gate_up", "lora_b_gate_up", "lora_a_down", "lora_b_down",
+        "token_lora_mapping", "stage_events")]
+
+
+NUM_STAGE_EVENTS = 7
+STAGE_NAMES = ("route_permute", "lora_shrink_gate_up", "gemm_gate_up_swiglu",
+               "lora_shrink_down", "gemm_down", "finalize")
+
+
+class MoELoRAError(RuntimeError):
+    pass
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the HIP library (no GPU needed to load it)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise MoELoRAError(
+            f"{path} is not built; run `python -m mixture_experts_layer_up_amd.build` "
+            "(or __graft_entry__.build()). There is no fallback implementation.")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    vp = ctypes.c_void_p
+    lib.moe_lora_workspace_size.argtypes = [P(Shape)]
+    lib.moe_lora_workspace_size.restype = ctypes.c_size_t
+    lib.moe_lora_packed_w13_bytes.argtypes = [P(Shape)]
+    lib.moe_lora_packed_w13_bytes.restype = ctypes.c_size_t
+    lib.moe_lora_packed_w2_bytes.argtypes = [P(Shape)]
+    lib.moe_lora_packed_w2_bytes.restype = ctypes.c_size_t
+    lib.moe_lora_pack_weights.argtypes = [P(Shape), vp, vp, vp, vp, vp]
+    lib.moe_lora_pack_weights.restype = ctypes.c_int
+    lib.moe_lora_route.argtypes = [P(Shape), vp, vp, vp, vp, P(Routing), vp]
+    lib.moe_lora_route.restype = ctypes.c_int
+    lib.moe_lora_forward.argtypes = [P(Shape), P(Inputs), P(Routing), vp, vp, ctypes.c_size_t, vp]
+    lib.moe_lora_forward.restype = ctypes.c_int
+    lib.moe_lora_strerror.argtypes = [ctypes.c_int]
+    lib.moe_lora_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def header_functions(path: str = HEADER_PATH):
+    """Names of the functions the public header declares."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_lora_[a-z0-9_]+)\s*\(", text)))
+
+
+def make_shape(cfg) -> Shape:
+    return Shape(cfg.num_tokens, cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k,
+                 cfg.local_expert_offset, cfg.local_num_experts, cfg.num_loras,
+                 cfg.rank_gate_up, cfg.rank_down, float(cfg.routed_scaling_factor))
+
+
+def _check(rc: int):
+    if rc != 0:
+        msg = load_library().moe_lora_strerror(rc).decode()
+        raise MoELoRAError(f"moe_lora call failed ({rc}): {msg}")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, shape: Optional[Sequence[int]] = None,
+         name: str = "tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise MoELoRAError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise MoELoRAError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise MoELoRAError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise MoELoRAError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def workspace_size(shape: Shape) -> int:
+    return int(load_library().moe_lora_workspace_size(ctypes.byref(shape)))
+
+
+def pack_weights(shape: Shape, w13: torch.Tensor, w2: torch.Tensor):
+    """Packed copies of w13 [E_l, H, 2I] and w2 [E_l, I, H] (bf16, device)."""
+    E_l, H, I = shape.local_num_experts, shape.hidden, shape.inter
+    w13p = torch.empty_like(w13)
+    w2p = torch.empty_like(w2)
+    _check(load_library().moe_lora_pack_weights(
+        ctypes.byref(shape), _ptr(w13, _BF16, (E_l, H, 2 * I), "w13"),
+        _ptr(w2, _BF16, (E_l, I, H), "w2"), w13p.data_ptr(), w2p.data_ptr(), _stream()))
+    return w13p, w2p
+
+
+def alloc_routing(shape: Shape, device) -> Dict[str, torch.Tensor]:
+    T, k, E_l, L = shape.num_tokens, shape.top_k, shape.local_num_experts, shape.num_loras
+    i32 = dict(dtype=torch.int32, device=device)
+    return {
+        "topk_ids": torch.empty((T, k), **i32),
+        "topk_weights": torch.empty((T, k), dtype=torch.float32, device=device),
+        "expert_counts": torch.empty(E_l, **i32),
+        "expert_offsets": torch.empty(E_l + 1, **i32),
+        "expanded_idx_to_permuted_idx": torch.empty(T * k, **i32),
+        "permuted_idx_to_expanded_idx": torch.empty(T * k, **i32),
+        "lora_seg_offsets": torch.empty(L * E_l + 1, **i32),
+        "lora_seg_slots": torch.empty(T * k, **i32),
+    }
+
+
+def _routing_struct(r: Dict[str, torch.Tensor]) -> Routing:
+    return Routing(*[r[name].data_ptr() if r.get(name) is not None else None
+                     for name, _ in Routing._fields_])
+
+
+def route(shape: Shape, router_logits: Optional[torch.Tensor] = None,
+          topk_ids: Optional[torch.Tensor] = None, topk_weights: Optional[torch.Tensor] = None,
+          token_lora_mapping: Optional[torch.Tensor] = None,
+          routing: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    T, E, k = shape.num_tokens, shape.num_experts, shape.top_k
+    dev = (router_logits if router_logits is not None else topk_ids).device
+    r = routing if routing is not None else alloc_routing(shape, dev)
+    rs = _routing_struct(r)
+    _check(load_library().moe_lora_route(
+        ctypes.byref(shape),
+        _ptr(router_logits, torch.float32, (T, E), "router_logits"),
+        _ptr(topk_ids, torch.int32, (T, k), "topk_ids"),
+        _ptr(topk_weights, torch.float32, (T, k), "topk_weights"),
+        _ptr(token_lora_mapping, torch.int32, (T,), "token_lora_mapping"),
+        ctypes.byref(rs), _stream()))
+    return r
+
+
+def forward(shape: Shape, hidden: torch.Tensor, w13_packed: torch.Tensor,
+            w2_packed: torch.Tensor, lora_a_gate_up=None, lora_b_gate_up=None,
+            lora_a_down=None, lora_b_down=None, token_lora_mapping=None,
+            router_logits=None, topk_ids=None, topk_weights=None,
+            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+            routing: Optional[Dict[str, torch.Tensor]] = None,
+            stage_events: Optional[Sequence[int]] = None) -> torch.Tensor:
+    """One layer forward on the current stream; returns ``out`` bf16 [T, H]."""
+    T, H, I, E, k = shape.num_tokens, shape.hidden, shape.inter, shape.num_experts, shape.top_k
+    E_l, L, rg, rd = shape.local_num_experts, shape.num_loras, shape.rank_gate_up, shape.rank_down
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=hidden.device)
+    ws_bytes = workspace_size(shape)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=hidden.device)
+    gu = L > 0 and rg > 0
+    dn = L > 0 and rd > 0
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != NUM_STAGE_EVENTS:
+            raise MoELoRAError(f"stage_events needs {NUM_STAGE_EVENTS} hipEvent_t handles")
+        ev = (ctypes.c_void_p * NUM_STAGE_EVENTS)(*stage_events)
+    inputs = Inputs(
+        _ptr(hidden, _BF16, (T, H), "hidden"),
+        _ptr(router_logits, torch.float32, (T, E), "router_logits"),
+        _ptr(topk_ids, torch.int32, (T, k), "topk_ids"),
+        _ptr(topk_weights, torch.float32, (T, k), "topk_weights"),
+        _ptr(w13_packed, _BF16, (E_l, H, 2 * I), "w13_packed"),
+        _ptr(w2_packed, _BF16, (E_l, I, H), "w2_packed"),
+        _ptr(lora_a_gate_up, _BF16, (L, E_l, rg, H), "lora_a_gate_up") if gu else None,
+        _ptr(lora_b_gate_up, _BF16, (L, E_l, 2 * I, rg), "lora_b_gate_up") if gu else None,
+        _ptr(lora_a_down, _BF16, (L, E_l, rd, I), "lora_a_down") if dn else None,
+        _ptr(lora_b_down, _BF16, (L, E_l, H, rd), "lora_b_down") if dn else None,
+        _ptr(token_lora_mapping, torch.int32, (T,), "token_lora_mapping"),
+        ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None,
+    )
+    rs = _routing_struct(routing) if routing is not None else None
+    _check(load_library().moe_lora_forward(
+        ctypes.byref(shape), ctypes.byref(inputs), ctypes.byref(rs) if rs is not None else None,
+        _ptr(out, _BF16, (T, H), "out"), _ptr(workspace, None, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return out
+
+
+def layer_from_host(cfg, inputs: Dict, device="cuda"):
+    """Upload host arrays from the input generator and pack the expert weights.
+
+    Returns a dict of device tensors keyed like the ``forward`` arguments.
+    """
+    import numpy as np
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+    shape = make_shape(cfg)
+    w13 = dev_bf16(inputs["w13"])
+    w2 = dev_bf16(inputs["w2"])
+    w13p, w2p = pack_weights(shape, w13, w2)
+    del w13, w2
+    L = cfg.num_loras
+    layer = {
+        "hidden": dev_bf16(inputs["hidden"]),
+        "router_logits": torch.from_numpy(inputs["logits"]).to(device),
+        "w13_packed": w13p,
+        "w2_packed": w2p,
+        "token_lora_mapping": torch.from_numpy(inputs["mapping"]).to(device),
+    }
+    if L > 0 and cfg.rank_gate_up > 0:
+        layer["lora_a_gate_up"] = dev_bf16(inputs["a_gu"])
+        layer["lora_b_gate_up"] = dev_bf16(inputs["b_gu"])
+    if L > 0 and cfg.rank_down > 0:
+        layer["lora_a_down"] = dev_bf16(inputs["a_dn"])
+        layer["lora_b_down"] = dev_bf16(inputs["b_dn"])
+    return shape, layer

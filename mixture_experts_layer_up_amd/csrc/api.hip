@@ -1,0 +1,380 @@
+// api.hip -- the C ABI: validation, workspace layout, stage sequencing.
+//
+// Stage order follows the pages' launcher: routing -> permute -> gate_up
+// GEMM -> LoRA-aware activation -> down GEMM -> finalize, with the gate_up
+// LoRA shrink/expand before the activation and the down LoRA after the down
+// GEMM ("BF16 support for the experimental_sgl_trtllm MoE-LoRA path",
+// "Files changed" table, launcher and single-stream dispatch rows, and Flow
+// section 1(A)).  Here the two LoRA expands run inside the GEMMs, the
+// activation is the gate_up GEMM's epilogue, and the down delta is summed
+// into y before the finalize applies the routing weight.
+//
+// Validation is pure host code and touches no HIP API, so it runs (and is
+// tested) on a machine without a GPU.  Forward never allocates and never
+// waits on the device.
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "kernels.h"
+#include "moe_lora.h"
+
+using namespace moe_lora;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int round8(int r) { return (r + 7) / 8 * 8; }
+
+int validate_shape(const moe_lora_shape *s)
+{
+    if (!s)
+        return MOE_LORA_ERR_INVALID_ARG;
+    if (s->num_tokens < 0 || s->top_k < 1 || s->top_k > 64 || s->num_experts < 1 ||
+        s->num_experts > 1024 || s->top_k > s->num_experts)
+        return MOE_LORA_ERR_UNSUPPORTED_SHAPE;
+    if ((int64_t)s->num_tokens * s->top_k > (int64_t)1 << 24)
+        return MOE_LORA_ERR_UNSUPPORTED_SHAPE;
+    if (s->hidden < 64 || s->hidden > 65536 || s->hidden % 64 != 0)
+        return MOE_LORA_ERR_UNSUPPORTED_SHAPE;
+    if (s->inter < 32 || s->inter > 65536 || s->inter % 32 != 0)
+        return MOE_LORA_ERR_UNSUPPORTED_SHAPE;
+    if (s->local_expert_offset < 0 || s->local_num_experts < 1 ||
+        (int64_t)s->local_expert_offset + s->local_num_experts > s->num_experts)
+        return MOE_LORA_ERR_UNSUPPORTED_SHAPE;
+    if (s->num_loras < 0 || s->num_loras > 64 ||
+        (int64_t)s->num_loras * s->local_num_experts > 8192)
+        return MOE_LORA_ERR_UNSUPPORTED_SHAPE;
+    if (s->rank_gate_up < 0 || s->rank_gate_up > 256 || s->rank_down < 0 || s->rank_down > 256)
+        return MOE_LORA_ERR_UNSUPPORTED_SHAPE;
+    if (!std::isfinite(s->routed_scaling_factor))
+        return MOE_LORA_ERR_INVALID_ARG;
+    return MOE_LORA_OK;
+}
+
+bool lora_gate_up_active(const moe_lora_shape *s) { return s->num_loras > 0 && s->rank_gate_up > 0; }
+bool lora_down_active(const moe_lora_shape *s) { return s->num_loras > 0 && s->rank_down > 0; }
+
+// Workspace regions; every offset is a multiple of 256 bytes.
+struct Layout {
+    size_t ids, weights, counts, offsets, exp2perm, perm2exp, seg_offsets, seg_slots;
+    size_t s_gu, act, s_dn, y;
+    size_t total;
+};
+
+Layout make_layout(const moe_lora_shape *s)
+{
+    const size_t n = (size_t)s->num_tokens * s->top_k;
+    const size_t el = (size_t)s->local_num_experts;
+    const size_t segs = (size_t)s->num_loras * el;
+    Layout L{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align_up(o + bytes, kAlign);
+        return at;
+    };
+    L.ids = take(n * 4);
+    L.weights = take(n * 4);
+    L.counts = take(el * 4);
+    L.offsets = take((el + 1) * 4);
+    L.exp2perm = take(n * 4);
+    L.perm2exp = take(n * 4);
+    L.seg_offsets = take((segs + 1) * 4);
+    L.seg_slots = take(n * 4);
+    L.s_gu = take(lora_gate_up_active(s) ? n * round8(s->rank_gate_up) * 2 : 0);
+    L.act = take(n * (size_t)s->inter * 2);
+    L.s_dn = take(lora_down_active(s) ? n * round8(s->rank_down) * 2 : 0);
+    L.y = take(n * (size_t)s->hidden * 2);
+    L.total = o;
+    return L;
+}
+
+int check(hipError_t e) { return e == hipSuccess ? MOE_LORA_OK : MOE_LORA_ERR_HIP; }
+
+#define MOE_TRY(expr)                  \
+    do {                               \
+        const int rc_ = (expr);        \
+        if (rc_ != MOE_LORA_OK)        \
+            return rc_;                \
+    } while (0)
+
+struct RoutingPtrs {
+    int32_t *ids;
+    float *weights;
+    int32_t *counts, *offsets, *exp2perm, *perm2exp, *seg_offsets, *seg_slots;
+};
+
+int enqueue_routing(const moe_lora_shape *s, const float *logits, const int32_t *topk_ids,
+                    const int32_t *mapping, const RoutingPtrs &r, hipStream_t st)
+{
+    if (logits) {
+        RouteArgs ra{logits, r.ids, r.weights, s->num_tokens, s->num_experts, s->top_k};
+        MOE_TRY(check(launch_route(ra, st)));
+    }
+    PermuteArgs pa{};
+    pa.topk_ids = logits ? r.ids : topk_ids;
+    pa.mapping = mapping;
+    pa.T = s->num_tokens;
+    pa.k = s->top_k;
+    pa.off = s->local_expert_offset;
+    pa.E_l = s->local_num_experts;
+    pa.L = s->num_loras;
+    pa.expert_counts = r.counts;
+    pa.expert_offsets = r.offsets;
+    pa.exp2perm = r.exp2perm;
+    pa.perm2exp = r.perm2exp;
+    pa.seg_offsets = r.seg_offsets;
+    pa.seg_slots = r.seg_slots;
+    return check(launch_permute(pa, st));
+}
+
+int record(void *const *events, int i, hipStream_t st)
+{
+    if (!events)
+        return MOE_LORA_OK;
+    return check(hipEventRecord(static_cast<hipEvent_t>(events[i]), st));
+}
+
+} // namespace
+
+extern "C" {
+
+size_t moe_lora_workspace_size(const moe_lora_shape *shape)
+{
+    if (validate_shape(shape) != MOE_LORA_OK)
+        return 0;
+    return make_layout(shape).total;
+}
+
+size_t moe_lora_packed_w13_bytes(const moe_lora_shape *shape)
+{
+    if (validate_shape(shape) != MOE_LORA_OK)
+        return 0;
+    return (size_t)shape->local_num_experts * shape->hidden * 2 * shape->inter * 2;
+}
+
+size_t moe_lora_packed_w2_bytes(const moe_lora_shape *shape)
+{
+    if (validate_shape(shape) != MOE_LORA_OK)
+        return 0;
+    return (size_t)shape->local_num_experts * shape->inter * shape->hidden * 2;
+}
+
+int moe_lora_pack_weights(const moe_lora_shape *shape, const void *w13, const void *w2,
+                          void *w13_packed, void *w2_packed, void *stream)
+{
+    MOE_TRY(validate_shape(shape));
+    if (!w13 || !w2 || !w13_packed || !w2_packed)
+        return MOE_LORA_ERR_INVALID_ARG;
+    if (!aligned(w13, 16) || !aligned(w2, 16) || !aligned(w13_packed, 16) || !aligned(w2_packed, 16))
+        return MOE_LORA_ERR_MISALIGNED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    PackArgs p13{static_cast<const uint16_t *>(w13), static_cast<uint16_t *>(w13_packed),
+                 shape->local_num_experts, shape->hidden, 2 * shape->inter, shape->inter};
+    MOE_TRY(check(launch_pack(p13, st)));
+    PackArgs p2{static_cast<const uint16_t *>(w2), static_cast<uint16_t *>(w2_packed),
+                shape->local_num_experts, shape->inter, shape->hidden, 0};
+    return check(launch_pack(p2, st));
+}
+
+int moe_lora_route(const moe_lora_shape *shape, const float *router_logits,
+                   const int32_t *topk_ids, const float *topk_weights,
+                   const int32_t *token_lora_mapping, const moe_lora_routing *routing,
+                   void *stream)
+{
+    MOE_TRY(validate_shape(shape));
+    if (!routing)
+        return MOE_LORA_ERR_INVALID_ARG;
+    const bool from_logits = router_logits != nullptr;
+    if (from_logits == (topk_ids != nullptr || topk_weights != nullptr))
+        return MOE_LORA_ERR_INVALID_ARG;
+    if (!from_logits && (!topk_ids || !topk_weights))
+        return MOE_LORA_ERR_INVALID_ARG;
+    if (from_logits && (!routing->topk_ids || !routing->topk_weights))
+        return MOE_LORA_ERR_INVALID_ARG;
+    if (!routing->expert_counts || !routing->expert_offsets ||
+        !routing->expanded_idx_to_permuted_idx || !routing->permuted_idx_to_expanded_idx ||
+        !routing->lora_seg_offsets || !routing->lora_seg_slots)
+        return MOE_LORA_ERR_INVALID_ARG;
+    RoutingPtrs r{routing->topk_ids, routing->topk_weights, routing->expert_counts,
+                  routing->expert_offsets, routing->expanded_idx_to_permuted_idx,
+                  routing->permuted_idx_to_expanded_idx, routing->lora_seg_offsets,
+                  routing->lora_seg_slots};
+    return enqueue_routing(shape, router_logits, topk_ids, token_lora_mapping, r,
+                           static_cast<hipStream_t>(stream));
+}
+
+int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
+                     const moe_lora_routing *routing, void *out, void *workspace,
+                     size_t workspace_bytes, void *stream)
+{
+    MOE_TRY(validate_shape(shape));
+    if (!in || !out || !workspace || !in->hidden || !in->w13_packed || !in->w2_packed)
+        return MOE_LORA_ERR_INVALID_ARG;
+    const bool from_logits = in->router_logits != nullptr;
+    if (from_logits == (in->topk_ids != nullptr || in->topk_weights != nullptr))
+        return MOE_LORA_ERR_INVALID_ARG;
+    if (!from_logits && (!in->topk_ids || !in->topk_weights))
+        return MOE_LORA_ERR_INVALID_ARG;
+    const bool gu = lora_gate_up_active(shape);
+    const bool dn = lora_down_active(shape);
+    if (gu && (!in->lora_a_gate_up || !in->lora_b_gate_up))
+        return MOE_LORA_ERR_INVALID_ARG;
+    if (dn && (!in->lora_a_down || !in->lora_b_down))
+        return MOE_LORA_ERR_INVALID_ARG;
+    if (!aligned(in->hidden, 16) || !aligned(in->w13_packed, 16) || !aligned(in->w2_packed, 16) ||
+        !aligned(out, 16) || !aligned(workspace, kAlign))
+        return MOE_LORA_ERR_MISALIGNED;
+    if (gu && (!aligned(in->lora_a_gate_up, 16) ||
+               !aligned(in->lora_b_gate_up, shape->rank_gate_up % 8 == 0 ? 16 : 2)))
+        return MOE_LORA_ERR_MISALIGNED;
+    if (dn && (!aligned(in->lora_a_down, 16) ||
+               !aligned(in->lora_b_down, shape->rank_down % 8 == 0 ? 16 : 2)))
+        return MOE_LORA_ERR_MISALIGNED;
+    if (routing && (!routing->expert_counts || !routing->expert_offsets ||
+                    !routing->expanded_idx_to_permuted_idx ||
+                    !routing->permuted_idx_to_expanded_idx || !routing->lora_seg_offsets ||
+                    !routing->lora_seg_slots ||
+                    (from_logits && (!routing->topk_ids || !routing->topk_weights))))
+        return MOE_LORA_ERR_INVALID_ARG;
+    const Layout lay = make_layout(shape);
+    if (workspace_bytes < lay.total)
+        return MOE_LORA_ERR_WORKSPACE_TOO_SMALL;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    RoutingPtrs r{};
+    if (routing) {
+        r = RoutingPtrs{routing->topk_ids, routing->topk_weights, routing->expert_counts,
+                        routing->expert_offsets, routing->expanded_idx_to_permuted_idx,
+                        routing->permuted_idx_to_expanded_idx, routing->lora_seg_offsets,
+                        routing->lora_seg_slots};
+        if (!from_logits) {
+            r.ids = nullptr;
+            r.weights = nullptr;
+        }
+    } else {
+        r = RoutingPtrs{reinterpret_cast<int32_t *>(ws + lay.ids),
+                        reinterpret_cast<float *>(ws + lay.weights),
+                        reinterpret_cast<int32_t *>(ws + lay.counts),
+                        reinterpret_cast<int32_t *>(ws + lay.offsets),
+                        reinterpret_cast<int32_t *>(ws + lay.exp2perm),
+                        reinterpret_cast<int32_t *>(ws + lay.perm2exp),
+                        reinterpret_cast<int32_t *>(ws + lay.seg_offsets),
+                        reinterpret_cast<int32_t *>(ws + lay.seg_slots)};
+    }
+    const float *weights = from_logits ? r.weights : in->topk_weights;
+    void *const *ev = in->stage_events;
+
+    const int T = shape->num_tokens, H = shape->hidden, I = shape->inter;
+    const int k = shape->top_k, E_l = shape->local_num_experts, L = shape->num_loras;
+    const int rg = shape->rank_gate_up, rd = shape->rank_down;
+    uint16_t *s_gu = reinterpret_cast<uint16_t *>(ws + lay.s_gu);
+    uint16_t *act = reinterpret_cast<uint16_t *>(ws + lay.act);
+    uint16_t *s_dn = reinterpret_cast<uint16_t *>(ws + lay.s_dn);
+    uint16_t *y = reinterpret_cast<uint16_t *>(ws + lay.y);
+    const uint16_t *hidden = static_cast<const uint16_t *>(in->hidden);
+
+    MOE_TRY(record(ev, 0, st));
+    MOE_TRY(enqueue_routing(shape, in->router_logits, in->topk_ids, in->token_lora_mapping, r, st));
+    MOE_TRY(record(ev, 1, st));
+    if (T == 0) {
+        for (int i = 2; i < MOE_LORA_NUM_STAGE_EVENTS; ++i)
+            MOE_TRY(record(ev, i, st));
+        return MOE_LORA_OK;
+    }
+
+    if (gu) {
+        ShrinkArgs sa{hidden, 1, H, static_cast<const uint16_t *>(in->lora_a_gate_up),
+                      rg, round8(rg), L, E_l, k, r.seg_offsets, r.seg_slots, r.exp2perm, s_gu};
+        MOE_TRY(check(launch_shrink(sa, st)));
+    }
+    MOE_TRY(record(ev, 2, st));
+
+    GemmArgs g1{};
+    g1.X = hidden;
+    g1.gather_by_token = 1;
+    g1.K = H;
+    g1.Wp = static_cast<const uint16_t *>(in->w13_packed);
+    g1.NT = 2 * I / 16;
+    g1.S = gu ? s_gu : nullptr;
+    g1.LB = gu ? static_cast<const uint16_t *>(in->lora_b_gate_up) : nullptr;
+    g1.r = gu ? rg : 0;
+    g1.rp = gu ? round8(rg) : 8;
+    g1.L = gu ? L : 0;
+    g1.n_canon = 2 * I;
+    g1.mapping = in->token_lora_mapping;
+    g1.offsets = r.offsets;
+    g1.perm2exp = r.perm2exp;
+    g1.E_l = E_l;
+    g1.k = k;
+    g1.I = I;
+    g1.Y = act;
+    g1.n_slabs = g1.NT / 4;
+    MOE_TRY(check(launch_gemm_gate_up(g1, st)));
+    MOE_TRY(record(ev, 3, st));
+
+    if (dn) {
+        ShrinkArgs sa{act, 0, I, static_cast<const uint16_t *>(in->lora_a_down),
+                      rd, round8(rd), L, E_l, k, r.seg_offsets, r.seg_slots, r.exp2perm, s_dn};
+        MOE_TRY(check(launch_shrink(sa, st)));
+    }
+    MOE_TRY(record(ev, 4, st));
+
+    GemmArgs g2{};
+    g2.X = act;
+    g2.gather_by_token = 0;
+    g2.K = I;
+    g2.Wp = static_cast<const uint16_t *>(in->w2_packed);
+    g2.NT = H / 16;
+    g2.S = dn ? s_dn : nullptr;
+    g2.LB = dn ? static_cast<const uint16_t *>(in->lora_b_down) : nullptr;
+    g2.r = dn ? rd : 0;
+    g2.rp = dn ? round8(rd) : 8;
+    g2.L = dn ? L : 0;
+    g2.n_canon = H;
+    g2.mapping = in->token_lora_mapping;
+    g2.offsets = r.offsets;
+    g2.perm2exp = r.perm2exp;
+    g2.E_l = E_l;
+    g2.k = k;
+    g2.I = I;
+    g2.Y = y;
+    g2.n_slabs = g2.NT / 4;
+    MOE_TRY(check(launch_gemm_down(g2, st)));
+    MOE_TRY(record(ev, 5, st));
+
+    FinalizeArgs fa{y, r.exp2perm, weights, static_cast<uint16_t *>(out), T, H, k,
+                    shape->routed_scaling_factor};
+    MOE_TRY(check(launch_finalize(fa, st)));
+    MOE_TRY(record(ev, 6, st));
+    return MOE_LORA_OK;
+}
+
+const char *moe_lora_strerror(int status)
+{
+    switch (status) {
+    case MOE_LORA_OK:
+        return "ok";
+    case MOE_LORA_ERR_INVALID_ARG:
+        return "invalid argument (null pointer or inconsistent inputs)";
+    case MOE_LORA_ERR_UNSUPPORTED_SHAPE:
+        return "unsupported shape (see limits in moe_lora.h)";
+    case MOE_LORA_ERR_WORKSPACE_TOO_SMALL:
+        return "workspace too small";
+    case MOE_LORA_ERR_MISALIGNED:
+        return "pointer not aligned as required";
+    case MOE_LORA_ERR_HIP:
+        return "HIP launch or event call failed";
+    default:
+        return "unknown status";
+    }
+}
+
+} // extern "C"

@@ -1,0 +1,73 @@
+// device_common.h -- small device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16)
+{
+    return __uint_as_float(bits16 << 16);
+}
+
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ u32x4 load16(const void *p)
+{
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+__device__ __forceinline__ void store16(void *p, u32x4 v)
+{
+    *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v)
+{
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ u32x4 zero16()
+{
+    u32x4 z = {0u, 0u, 0u, 0u};
+    return z;
+}
+
+// D = A * B + C for a 16x16 tile with K = 32 (bf16 in, fp32 accumulate).
+// Lane l holds A[l % 16][8(l / 16) .. +7], B[8(l / 16) .. +7][l % 16] and
+// D[4(l / 16) .. +3][l % 16].
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Blocks are dispatched round-robin over the 8 XCDs (block b runs on XCD
+// b % 8).  Renumber so that each XCD receives one contiguous range of
+// logical work items: neighbouring items (for example the column slabs of
+// one expert, which share activation rows) then share that XCD's L2.
+__device__ __forceinline__ int xcd_contiguous_index(int bid, int n)
+{
+    const int xcd = bid & 7;
+    const int idx = bid >> 3;
+    const int per = n >> 3;
+    const int rem = n & 7;
+    return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}
+
+__device__ __forceinline__ float silu_f32(float z)
+{
+    return z / (1.0f + expf(-z));
+}

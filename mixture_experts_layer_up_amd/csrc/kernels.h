@@ -1,0 +1,79 @@
+// kernels.h -- argument blocks and host launchers of the gfx950 kernels.
+// Internal to the library; the public interface is include/moe_lora.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe_lora {
+
+struct RouteArgs {
+    const float *logits;   // [T, E]
+    int32_t *topk_ids;     // [T, k]
+    float *topk_weights;   // [T, k]
+    int T, E, k;
+};
+
+struct PermuteArgs {
+    const int32_t *topk_ids;   // [T*k]
+    const int32_t *mapping;    // [T] or null
+    int T, k, off, E_l, L;
+    int32_t *expert_counts, *expert_offsets;
+    int32_t *exp2perm, *perm2exp;
+    int32_t *seg_offsets, *seg_slots;
+};
+
+struct PackArgs {
+    const uint16_t *src;   // [E_l, K, N]
+    uint16_t *dst;
+    int E_l, K, N, I;      // I > 0: gate/up interleaved tile order (w13)
+};
+
+// LoRA shrink S[p] = A[l, e] * X(row), grouped by (adapter, local expert).
+struct ShrinkArgs {
+    const uint16_t *X;        // gather_by_token ? hidden [T, K] : act [n, K]
+    int gather_by_token;
+    int K;
+    const uint16_t *A;        // [L, E_l, r, K]
+    int r, rp, L, E_l, k;
+    const int32_t *seg_offsets, *seg_slots, *exp2perm;
+    uint16_t *S;              // [n, rp], row = permuted index
+};
+
+// Grouped expert GEMM over one packed weight stack, with the LoRA expand
+// folded in as extra K (S [n, rp] against the LoRA B stack).
+struct GemmArgs {
+    const uint16_t *X;        // gather_by_token ? hidden [T, K] : act [n, K]
+    int gather_by_token;
+    int K;                    // H for gate_up, I for down
+    const uint16_t *Wp;       // packed [E_l, NT, K/32, 64, 8]
+    int NT;                   // 16-column tiles per expert
+    const uint16_t *S;        // [n, rp] or null
+    const uint16_t *LB;       // [L, E_l, n_canon, r] or null
+    int r, rp, L, n_canon;
+    const int32_t *mapping;   // [T] or null
+    const int32_t *offsets;   // [E_l + 1]
+    const int32_t *perm2exp;  // [n]
+    int E_l, k, I;
+    uint16_t *Y;              // gated: act [n, I]; else y [n, n_canon]
+    int n_slabs;
+};
+
+struct FinalizeArgs {
+    const uint16_t *Y;        // [n, H]
+    const int32_t *exp2perm;  // [T*k]
+    const float *weights;     // [T, k]
+    uint16_t *out;            // [T, H]
+    int T, H, k;
+    float scale;
+};
+
+hipError_t launch_route(const RouteArgs &a, hipStream_t s);
+hipError_t launch_permute(const PermuteArgs &a, hipStream_t s);
+hipError_t launch_pack(const PackArgs &a, hipStream_t s);
+hipError_t launch_shrink(const ShrinkArgs &a, hipStream_t s);
+hipError_t launch_gemm_gate_up(const GemmArgs &a, hipStream_t s);
+hipError_t launch_gemm_down(const GemmArgs &a, hipStream_t s);
+hipError_t launch_finalize(const FinalizeArgs &a, hipStream_t s);
+
+} // namespace moe_lora

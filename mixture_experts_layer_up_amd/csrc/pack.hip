@@ -1,0 +1,57 @@
+// pack.hip -- one-time relayout of expert weights into MFMA fragments.
+//
+// A [K, N] weight (N contiguous) is rewritten so that the B operand of one
+// 16x16x32 bf16 MFMA -- 32 K rows by 16 columns, lane l holding the 8
+// consecutive K values of column l % 16 starting at row 8 (l / 16) -- is
+// one contiguous 1 KiB block.  The grouped GEMMs then stream each expert's
+// weights with fully coalesced 16-byte loads straight into registers.
+//
+// For w13 the 16-column tiles alternate gate and up tiles of the same
+// columns (tile 2j = gate columns [16j, 16j+16), tile 2j+1 = the matching up
+// columns at I + 16j), so one block of the gate_up GEMM owns matching gate
+// and up outputs and can apply SwiGLU in its epilogue.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe_lora {
+namespace {
+
+__global__ __launch_bounds__(256) void pack_kernel(PackArgs a)
+{
+    const size_t f = (size_t)blockIdx.x * 256 + threadIdx.x;  // one 16-byte lane fragment
+    const int KC = a.K >> 5;
+    const int NT = a.N >> 4;
+    const size_t total = (size_t)a.E_l * NT * KC * kWave;
+    if (f >= total)
+        return;
+    const int lane = (int)(f & (kWave - 1));
+    size_t rest = f >> 6;
+    const int kc = (int)(rest % KC);
+    rest /= KC;
+    const int nt = (int)(rest % NT);
+    const int e = (int)(rest / NT);
+    const int col = a.I > 0 ? (nt & 1) * a.I + (nt >> 1) * 16 + (lane & 15)
+                            : nt * 16 + (lane & 15);
+    const int k0 = kc * 32 + (lane >> 4) * 8;
+    const uint16_t *src = a.src + ((size_t)e * a.K + k0) * a.N + col;
+    u32x4 v;
+    v.x = (uint32_t)src[0] | ((uint32_t)src[(size_t)1 * a.N] << 16);
+    v.y = (uint32_t)src[(size_t)2 * a.N] | ((uint32_t)src[(size_t)3 * a.N] << 16);
+    v.z = (uint32_t)src[(size_t)4 * a.N] | ((uint32_t)src[(size_t)5 * a.N] << 16);
+    v.w = (uint32_t)src[(size_t)6 * a.N] | ((uint32_t)src[(size_t)7 * a.N] << 16);
+    store16(a.dst + f * 8, v);
+}
+
+} // namespace
+
+hipError_t launch_pack(const PackArgs &a, hipStream_t s)
+{
+    const size_t total = (size_t)a.E_l * (a.N >> 4) * (a.K >> 5) * kWave;
+    if (total == 0)
+        return hipSuccess;
+    const size_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+} // namespace moe_lora

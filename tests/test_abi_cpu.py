@@ -1,0 +1,138 @@
+"""The C ABI on a machine without a GPU: load, symbols, pure host logic.
+
+No test here enqueues device work.  Every call below either is pure host code
+(workspace sizing) or must be rejected by host-side validation before any HIP
+call is made.
+"""
+import ctypes
+import os
+
+import pytest
+
+from mixture_experts_layer_up_amd import binding
+from mixture_experts_layer_up_amd.synth import CONFIGS
+
+ERR_INVALID_ARG, ERR_SHAPE, ERR_WS, ERR_ALIGN = -1, -2, -3, -4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from mixture_experts_layer_up_amd import build
+        build.build(verbose=False)
+    return binding.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = binding.header_functions()
+    assert {"moe_lora_route", "moe_lora_forward", "moe_lora_workspace_size",
+            "moe_lora_pack_weights", "moe_lora_strerror"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in moe_lora.h but not exported"
+
+
+def test_strerror(lib):
+    assert lib.moe_lora_strerror(0) == b"ok"
+    for rc in (-1, -2, -3, -4, -5):
+        assert lib.moe_lora_strerror(rc) not in (b"ok", b"unknown status")
+    assert lib.moe_lora_strerror(42) == b"unknown status"
+
+
+def _ws(cfg):
+    return binding.workspace_size(binding.make_shape(cfg))
+
+
+def test_workspace_size_is_pure_and_monotone(lib):
+    small = _ws(CONFIGS["tiny"])
+    assert small > 0 and small % 256 == 0
+    assert _ws(CONFIGS["tiny"]) == small
+    assert _ws(CONFIGS["prefill"]) > _ws(CONFIGS["decode64"]) > _ws(CONFIGS["decode16"])
+    # T * k * (H + I) bf16 rows dominate: y [T*k, H] and act [T*k, I]
+    c = CONFIGS["prefill"]
+    n = c.num_tokens * c.top_k
+    assert _ws(c) >= n * (c.hidden + c.inter) * 2
+    # no adapters -> no LoRA scratch
+    assert _ws(c.replace(num_loras=0)) < _ws(c)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("hidden", 96), ("hidden", 0), ("inter", 48), ("num_experts", 2048), ("top_k", 0),
+    ("top_k", 65), ("local_num_experts", 0), ("local_expert_offset", 120),
+    ("num_loras", 65), ("rank_gate_up", 300), ("num_tokens", -1)])
+def test_invalid_shapes_rejected(lib, field, value):
+    cfg = CONFIGS["decode64"].replace(**{field: value})
+    assert _ws(cfg) == 0
+    shape = binding.make_shape(cfg)
+    rs = binding.Routing()
+    assert lib.moe_lora_route(ctypes.byref(shape), ctypes.c_void_p(256), None, None, None,
+                              ctypes.byref(rs), None) == ERR_SHAPE
+
+
+def _fake(addr=4096):
+    return ctypes.c_void_p(addr)   # never dereferenced: validation rejects first
+
+
+def _inputs(**over):
+    base = dict(hidden=_fake(), router_logits=_fake(), topk_ids=None, topk_weights=None,
+                w13_packed=_fake(), w2_packed=_fake(), lora_a_gate_up=_fake(),
+                lora_b_gate_up=_fake(), lora_a_down=_fake(), lora_b_down=_fake(),
+                token_lora_mapping=_fake(), stage_events=None)
+    base.update(over)
+    return binding.Inputs(*[base[n] for n, _ in binding.Inputs._fields_])
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(hidden=None), ERR_INVALID_ARG),
+    (dict(router_logits=None), ERR_INVALID_ARG),                         # no routing source
+    (dict(topk_ids=_fake(), topk_weights=_fake()), ERR_INVALID_ARG),     # both sources
+    (dict(router_logits=None, topk_ids=_fake()), ERR_INVALID_ARG),       # ids without weights
+    (dict(lora_b_down=None), ERR_INVALID_ARG),                           # active LoRA, no stack
+    (dict(w2_packed=None), ERR_INVALID_ARG),
+    (dict(hidden=_fake(4096 + 8)), ERR_ALIGN),
+    (dict(lora_a_gate_up=_fake(4096 + 2)), ERR_ALIGN),
+])
+def test_forward_argument_validation(lib, over, expect):
+    shape = binding.make_shape(CONFIGS["decode64"])
+    inp = _inputs(**over)
+    ws = binding.workspace_size(shape)
+    rc = lib.moe_lora_forward(ctypes.byref(shape), ctypes.byref(inp), None, _fake(),
+                              _fake(1 << 20), ws, None)
+    assert rc == expect
+
+
+def test_forward_workspace_checks(lib):
+    shape = binding.make_shape(CONFIGS["decode64"])
+    ws = binding.workspace_size(shape)
+    inp = _inputs()
+    assert lib.moe_lora_forward(ctypes.byref(shape), ctypes.byref(inp), None, _fake(),
+                                _fake(1 << 20), ws - 1, None) == ERR_WS
+    assert lib.moe_lora_forward(ctypes.byref(shape), ctypes.byref(inp), None, _fake(),
+                                _fake((1 << 20) + 16), ws, None) == ERR_ALIGN
+    assert lib.moe_lora_forward(None, ctypes.byref(inp), None, _fake(), _fake(1 << 20), ws,
+                                None) == ERR_INVALID_ARG
+
+
+def test_lora_pointers_optional_when_inactive(lib):
+    # with no adapters the LoRA pointers may be NULL; validation must then get as far
+    # as the workspace check (given a too-small workspace, so nothing is launched)
+    shape = binding.make_shape(CONFIGS["decode64"].replace(num_loras=0))
+    inp = _inputs(lora_a_gate_up=None, lora_b_gate_up=None, lora_a_down=None,
+                  lora_b_down=None)
+    ws = binding.workspace_size(shape)
+    assert lib.moe_lora_forward(ctypes.byref(shape), ctypes.byref(inp), None, _fake(),
+                                _fake(1 << 20), ws - 256, None) == ERR_WS
+
+
+def test_route_and_pack_validation(lib):
+    shape = binding.make_shape(CONFIGS["tiny"])
+    rs = binding.Routing()   # all NULL
+    assert lib.moe_lora_route(ctypes.byref(shape), _fake(), None, None, None,
+                              ctypes.byref(rs), None) == ERR_INVALID_ARG
+    assert lib.moe_lora_route(ctypes.byref(shape), None, None, None, None,
+                              None, None) == ERR_INVALID_ARG
+    assert lib.moe_lora_pack_weights(ctypes.byref(shape), None, _fake(), _fake(), _fake(),
+                                     None) == ERR_INVALID_ARG
+    assert lib.moe_lora_pack_weights(ctypes.byref(shape), _fake(4097), _fake(), _fake(),
+                                     _fake(), None) == ERR_ALIGN
+    assert lib.moe_lora_packed_w13_bytes(ctypes.byref(shape)) == 8 * 128 * 128 * 2
+    assert lib.moe_lora_packed_w2_bytes(ctypes.byref(shape)) == 8 * 64 * 128 * 2

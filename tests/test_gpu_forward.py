@@ -1,0 +1,189 @@
+"""Layer forward on the GPU against the fp64 CPU oracle.
+
+Bound: max|gpu - oracle| <= 1e-2 * max|oracle| + 1e-3 (bf16 output, fp32
+accumulation, bf16 intermediates for the LoRA shrink output, the activation
+and the per-slot expert output).  Where the LoRA contribution is too small to
+be seen under that bound, amplified-LoRA variants check the LoRA delta
+(out - out without adapters) on its own.
+"""
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_up_amd import binding
+from mixture_experts_layer_up_amd.synth import CONFIGS, LayerConfig, make_inputs
+from oracle import oracle
+from tests._gpu import announce, cached_inputs, run_forward, tol
+
+pytestmark = pytest.mark.gpu
+
+# Small shapes that still span several tiles and a ragged tail: 37 tokens,
+# H = 320 (5 column slabs of 64 in the down GEMM), I = 96 (3 gate/up slabs,
+# 3 K chunks in the down GEMM), ranks that are not multiples of 8 or 16.
+MID = LayerConfig("mid", 37, 320, 96, 16, 4, 0, 16, 3, 12, 8, seed=31, mapping="uniform",
+                  sigma_lora_a=0.2, sigma_lora_b=0.2)
+MID_R64 = MID.replace(name="mid_r64", rank_gate_up=64, rank_down=64, seed=32,
+                      sigma_lora_a=0.05, sigma_lora_b=0.05)
+MID_EP = MID.replace(name="mid_ep", local_expert_offset=5, local_num_experts=7, seed=33)
+# every expert gets > 64 rows, so the GEMMs take several row passes
+BIG_ROWS = LayerConfig("big_rows", 300, 128, 64, 4, 1, 0, 4, 2, 16, 16, seed=34,
+                       mapping="uniform", sigma_lora_a=0.2, sigma_lora_b=0.2)
+TINY_AMP = CONFIGS["tiny"].replace(name="tiny_amp", sigma_lora_a=0.2, sigma_lora_b=0.2)
+
+
+def _compare(cfg, inp, got, tokens=None, **kw):
+    ref = oracle.forward(cfg, inp, tokens=tokens, **kw)
+    sel = got if tokens is None else got[tokens]
+    err = np.abs(sel - ref).max(initial=0.0)
+    bound = tol(ref)
+    assert err <= bound, f"{cfg.name}: max err {err:.3e} > bound {bound:.3e}"
+    return ref
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode16", "decode64", "ep_shard"])
+def test_layer_configs_match_oracle(name):
+    announce(f"forward {name}")
+    cfg = CONFIGS[name]
+    inp = cached_inputs(name)
+    got, _ = run_forward(cfg, inp)
+    _compare(cfg, inp, got)
+
+
+def test_prefill_sampled_tokens():
+    announce("forward prefill (sampled rows)")
+    cfg = CONFIGS["prefill"]
+    inp = cached_inputs("prefill")
+    got, _ = run_forward(cfg, inp)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(55)
+    # 16 rows from each of the four adapter runs, plus the first and last token
+    toks = np.concatenate([[0, cfg.num_tokens - 1]] +
+                          [rng.choice(np.arange(a * 512, (a + 1) * 512), 16, replace=False)
+                           for a in range(4)]).astype(np.int32)
+    _compare(cfg, inp, got, tokens=toks)
+
+
+@pytest.mark.parametrize("cfg", [MID, MID_R64, MID_EP, BIG_ROWS, TINY_AMP],
+                         ids=lambda c: c.name)
+def test_small_shapes_and_lora_delta(cfg):
+    announce(f"forward {cfg.name}")
+    inp = make_inputs(cfg)
+    got, _ = run_forward(cfg, inp)
+    ref = _compare(cfg, inp, got)
+    base_cfg = cfg.replace(num_loras=0)
+    got_base, _ = run_forward(base_cfg, inp)
+    ref_base = oracle.forward(base_cfg, inp)
+    d_ref = ref - ref_base
+    d_got = got - got_base
+    err = np.abs(d_got - d_ref).max()
+    # the delta is far above the base bound, so a wrong LoRA term cannot hide
+    assert np.abs(d_ref).max() > 10 * tol(ref_base)
+    # 1% of the delta, plus one bf16 rounding of each of the two outputs
+    bound = 1e-2 * np.abs(d_ref).max() + 2 ** -7 * np.abs(ref).max()
+    assert err <= bound, f"{cfg.name}: LoRA delta err {err:.3e} > {bound:.3e}"
+
+
+def test_no_adapter_paths_equal_base_bitwise():
+    announce("forward: no-adapter paths")
+    cfg = MID
+    inp = make_inputs(cfg)
+    base, _ = run_forward(cfg.replace(num_loras=0), inp)
+    none_mapped, _ = run_forward(cfg, inp, mapping=np.full(cfg.num_tokens, -1, np.int32))
+    np.testing.assert_array_equal(none_mapped, base)
+    no_mapping, _ = run_forward(cfg, inp, mapping=None)
+    np.testing.assert_array_equal(no_mapping, base)
+    out_of_range, _ = run_forward(cfg, inp, mapping=np.full(cfg.num_tokens, 7, np.int32))
+    np.testing.assert_array_equal(out_of_range, base)
+    z = dict(inp)
+    z["b_gu"] = np.zeros_like(inp["b_gu"])
+    z["b_dn"] = np.zeros_like(inp["b_dn"])
+    zero_b, _ = run_forward(cfg, z)
+    np.testing.assert_array_equal(zero_b, base)
+    r0, _ = run_forward(cfg.replace(rank_gate_up=0, rank_down=0), inp)
+    np.testing.assert_array_equal(r0, base)
+    _compare(cfg.replace(num_loras=0), inp, base)
+
+
+def test_topk_passthrough_with_invalid_slots():
+    announce("forward: top-k passthrough")
+    cfg = MID
+    inp = make_inputs(cfg)
+    ids, w = oracle.route(inp["logits"], cfg.top_k)
+    ids = ids.copy()
+    ids[0, 1] = -1
+    ids[3, 0] = 999
+    ids[5, :] = -1          # a token with no slot at all -> zero row
+    w32 = w.astype(np.float32)
+    got, _ = run_forward(cfg, inp, use_logits=False, topk=(ids, w32))
+    _compare(cfg, inp, got, topk_ids=ids, topk_weights=w32.astype(np.float64))
+    assert np.all(got[5] == 0)
+
+
+def test_expert_parallel_offsets_and_shard_sum():
+    full_cfg = MID.replace(name="ep_full", num_experts=16, local_num_experts=16)
+    inp_full = make_inputs(full_cfg)
+    ref_full = oracle.forward(full_cfg, inp_full)
+    total = np.zeros_like(ref_full)
+    for off in (0, 4, 8, 12):
+        announce(f"forward: EP shard off={off}")
+        cfg = full_cfg.replace(local_expert_offset=off, local_num_experts=4)
+        inp = make_inputs(cfg)
+        got, r = run_forward(cfg, inp, routing=True)
+        _compare(cfg, inp, got)
+        total += got
+        ids, _ = oracle.route(inp["logits"], cfg.top_k)
+        perm = oracle.permute(ids, inp["mapping"], 16, off, 4, cfg.num_loras)
+        for name in perm:
+            np.testing.assert_array_equal(r[name], perm[name], err_msg=name)
+    assert np.abs(total - ref_full).max() <= tol(ref_full, rel=2e-2)
+
+
+def test_routing_export_and_determinism():
+    announce("forward: routing export, determinism")
+    cfg = CONFIGS["decode64"]
+    inp = cached_inputs("decode64")
+    layer = binding.layer_from_host(cfg, inp)
+    a, ra = run_forward(cfg, inp, routing=True, layer=layer)
+    b, rb = run_forward(cfg, inp, routing=True, layer=layer)
+    np.testing.assert_array_equal(a, b)                    # bitwise run-to-run
+    ids, w = oracle.route(inp["logits"], cfg.top_k)
+    np.testing.assert_array_equal(ra["topk_ids"], ids)
+    np.testing.assert_allclose(ra["topk_weights"], w, rtol=1e-6)
+    perm = oracle.permute(ids, inp["mapping"], 128, 0, 128, 4)
+    for name in perm:
+        np.testing.assert_array_equal(ra[name], perm[name], err_msg=name)
+        np.testing.assert_array_equal(rb[name], perm[name], err_msg=name)
+
+
+def test_output_and_workspace_canaries():
+    """Every output row is written; nothing outside out / workspace changes."""
+    announce("forward: canaries")
+    cfg = MID_EP
+    inp = make_inputs(cfg)
+    shape, layer = binding.layer_from_host(cfg, inp)
+    T, H = cfg.num_tokens, cfg.hidden
+    guard = 4096
+    out_buf = torch.full((T * H + 2 * guard,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = out_buf[guard:guard + T * H].view(T, H)
+    ws_bytes = binding.workspace_size(shape)
+    ws_buf = torch.full((ws_bytes + 2 * guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    ws = ws_buf[guard:guard + ws_bytes]
+    assert ws.data_ptr() % 256 == 0
+    got, _ = run_forward(cfg, inp, layer=(shape, layer), out=out, workspace=ws)
+    assert np.isfinite(got).all()
+    ob = out_buf.float().cpu().numpy()
+    assert np.isnan(ob[:guard]).all() and np.isnan(ob[guard + T * H:]).all()
+    wb = ws_buf.cpu().numpy()
+    assert (wb[:guard] == 0x5A).all() and (wb[guard + ws_bytes:] == 0x5A).all()
+    _compare(cfg, inp, got)
+
+
+def test_scaling_factor_and_tiny_batches():
+    for T in (1, 2, 0):
+        announce(f"forward: T={T}")
+        cfg = MID.replace(num_tokens=T, routed_scaling_factor=0.5, seed=40 + T)
+        inp = make_inputs(cfg)
+        got, _ = run_forward(cfg, inp)
+        assert got.shape == (T, cfg.hidden)
+        if T:
+            _compare(cfg, inp, got)

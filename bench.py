@@ -158,6 +158,9 @@ def main():
     ap.add_argument("--workload", default="decode64", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle baseline time budget (0 = skip)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain copy kernel (torch.neg) over this many MiB, "
+                         "to calibrate HBM byte counters against a known size")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -183,6 +186,15 @@ def main():
     def step(events=None):
         binding.forward(shape, lay["hidden"], lay["w13_packed"], lay["w2_packed"], out=out,
                         workspace=ws, stage_events=events, **kw)
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: read {args.copy_probe_mib} MiB, wrote {args.copy_probe_mib} MiB")
+        del src, dst
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):

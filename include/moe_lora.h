@@ -27,6 +27,9 @@
  *     are safe when they use distinct outputs and workspaces.
  *   - Host-side validation needs no GPU: bad arguments return a negative
  *     status before any HIP call.  No entry point throws.
+ *   - An empty batch (num_tokens == 0) is valid: per-token and per-slot
+ *     pointers may then be NULL, nothing but the zero per-expert /
+ *     per-segment counts and offsets of `routing` (when given) is written.
  *   - Device data that is out of range never faults: a top-k id outside
  *     [local_expert_offset, local_expert_offset + local_num_experts) is a
  *     non-local slot (contributes nothing), and a token_lora_mapping value

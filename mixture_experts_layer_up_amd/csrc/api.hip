@@ -134,6 +134,26 @@ int enqueue_routing(const moe_lora_shape *s, const float *logits, const int32_t 
     return check(launch_permute(pa, st));
 }
 
+// An empty batch: only the per-expert / per-segment arrays have entries; they
+// are all zero.  Per-slot pointers may be NULL (empty tensors).
+int enqueue_empty_batch(const moe_lora_shape *s, const moe_lora_routing *routing, hipStream_t st)
+{
+    if (!routing)
+        return MOE_LORA_OK;
+    if (!routing->expert_counts || !routing->expert_offsets || !routing->lora_seg_offsets)
+        return MOE_LORA_ERR_INVALID_ARG;
+    PermuteArgs pa{};
+    pa.T = 0;
+    pa.k = s->top_k;
+    pa.off = s->local_expert_offset;
+    pa.E_l = s->local_num_experts;
+    pa.L = s->num_loras;
+    pa.expert_counts = routing->expert_counts;
+    pa.expert_offsets = routing->expert_offsets;
+    pa.seg_offsets = routing->lora_seg_offsets;
+    return check(launch_permute(pa, st));
+}
+
 int record(void *const *events, int i, hipStream_t st)
 {
     if (!events)
@@ -191,6 +211,8 @@ int moe_lora_route(const moe_lora_shape *shape, const float *router_logits,
     MOE_TRY(validate_shape(shape));
     if (!routing)
         return MOE_LORA_ERR_INVALID_ARG;
+    if (shape->num_tokens == 0)
+        return enqueue_empty_batch(shape, routing, static_cast<hipStream_t>(stream));
     const bool from_logits = router_logits != nullptr;
     if (from_logits == (topk_ids != nullptr || topk_weights != nullptr))
         return MOE_LORA_ERR_INVALID_ARG;
@@ -215,7 +237,16 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
                      size_t workspace_bytes, void *stream)
 {
     MOE_TRY(validate_shape(shape));
-    if (!in || !out || !workspace || !in->hidden || !in->w13_packed || !in->w2_packed)
+    if (!in)
+        return MOE_LORA_ERR_INVALID_ARG;
+    if (shape->num_tokens == 0) {
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        MOE_TRY(enqueue_empty_batch(shape, routing, st));
+        for (int i = 0; i < MOE_LORA_NUM_STAGE_EVENTS; ++i)
+            MOE_TRY(record(in->stage_events, i, st));
+        return MOE_LORA_OK;
+    }
+    if (!out || !workspace || !in->hidden || !in->w13_packed || !in->w2_packed)
         return MOE_LORA_ERR_INVALID_ARG;
     const bool from_logits = in->router_logits != nullptr;
     if (from_logits == (in->topk_ids != nullptr || in->topk_weights != nullptr))
@@ -284,11 +315,6 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     MOE_TRY(record(ev, 0, st));
     MOE_TRY(enqueue_routing(shape, in->router_logits, in->topk_ids, in->token_lora_mapping, r, st));
     MOE_TRY(record(ev, 1, st));
-    if (T == 0) {
-        for (int i = 2; i < MOE_LORA_NUM_STAGE_EVENTS; ++i)
-            MOE_TRY(record(ev, i, st));
-        return MOE_LORA_OK;
-    }
 
     if (gu) {
         ShrinkArgs sa{hidden, 1, H, static_cast<const uint16_t *>(in->lora_a_gate_up),

@@ -43,7 +43,7 @@ def run_forward(cfg, inputs, *, use_logits=True, topk=None, mapping="given",
         ids, w = topk
         kw["topk_ids"] = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
         kw["topk_weights"] = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).cuda()
-    if mapping == "given":
+    if isinstance(mapping, str) and mapping == "given":
         kw["token_lora_mapping"] = lay["token_lora_mapping"]
     elif mapping is not None:
         kw["token_lora_mapping"] = torch.from_numpy(np.asarray(mapping, np.int32)).cuda()

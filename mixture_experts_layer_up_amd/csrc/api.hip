@@ -63,7 +63,8 @@ bool lora_down_active(const moe_lora_shape *s) { return s->num_loras > 0 && s->r
 // Workspace regions; every offset is a multiple of 256 bytes.
 struct Layout {
     size_t ids, weights, counts, offsets, exp2perm, perm2exp, seg_offsets, seg_slots;
-    size_t s_gu, act, s_dn, y;
+    size_t tiles, s_gu, act, s_dn, y;
+    int tile_rows, max_tiles;
     size_t total;
 };
 
@@ -87,6 +88,9 @@ Layout make_layout(const moe_lora_shape *s)
     L.perm2exp = take(n * 4);
     L.seg_offsets = take((segs + 1) * 4);
     L.seg_slots = take(n * 4);
+    L.tile_rows = gemm_tile_rows((int)n, (int)el);
+    L.max_tiles = max_gemm_tiles((int)n, (int)el, L.tile_rows);
+    L.tiles = take((size_t)L.max_tiles * sizeof(int4));
     L.s_gu = take(lora_gate_up_active(s) ? n * round8(s->rank_gate_up) * 2 : 0);
     L.act = take(n * (size_t)s->inter * 2);
     L.s_dn = take(lora_down_active(s) ? n * round8(s->rank_down) * 2 : 0);
@@ -111,7 +115,8 @@ struct RoutingPtrs {
 };
 
 int enqueue_routing(const moe_lora_shape *s, const float *logits, const int32_t *topk_ids,
-                    const int32_t *mapping, const RoutingPtrs &r, hipStream_t st)
+                    const int32_t *mapping, const RoutingPtrs &r, hipStream_t st,
+                    int4 *tiles = nullptr, int tile_rows = 0, int max_tiles = 0)
 {
     if (logits) {
         RouteArgs ra{logits, r.ids, r.weights, s->num_tokens, s->num_experts, s->top_k};
@@ -131,6 +136,9 @@ int enqueue_routing(const moe_lora_shape *s, const float *logits, const int32_t 
     pa.perm2exp = r.perm2exp;
     pa.seg_offsets = r.seg_offsets;
     pa.seg_slots = r.seg_slots;
+    pa.tiles = tiles;
+    pa.tile_rows = tile_rows;
+    pa.max_tiles = max_tiles;
     return check(launch_permute(pa, st));
 }
 
@@ -313,7 +321,9 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     const uint16_t *hidden = static_cast<const uint16_t *>(in->hidden);
 
     MOE_TRY(record(ev, 0, st));
-    MOE_TRY(enqueue_routing(shape, in->router_logits, in->topk_ids, in->token_lora_mapping, r, st));
+    int4 *tiles = reinterpret_cast<int4 *>(ws + lay.tiles);
+    MOE_TRY(enqueue_routing(shape, in->router_logits, in->topk_ids, in->token_lora_mapping, r, st,
+                            tiles, lay.tile_rows, lay.max_tiles));
     MOE_TRY(record(ev, 1, st));
 
     if (gu) {
@@ -336,7 +346,9 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     g1.L = gu ? L : 0;
     g1.n_canon = 2 * I;
     g1.mapping = in->token_lora_mapping;
-    g1.offsets = r.offsets;
+    g1.tiles = tiles;
+    g1.n_tiles = lay.max_tiles;
+    g1.tile_rows = lay.tile_rows;
     g1.perm2exp = r.perm2exp;
     g1.E_l = E_l;
     g1.k = k;
@@ -366,7 +378,9 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     g2.L = dn ? L : 0;
     g2.n_canon = H;
     g2.mapping = in->token_lora_mapping;
-    g2.offsets = r.offsets;
+    g2.tiles = tiles;
+    g2.n_tiles = lay.max_tiles;
+    g2.tile_rows = lay.tile_rows;
     g2.perm2exp = r.perm2exp;
     g2.E_l = E_l;
     g2.k = k;

@@ -54,6 +54,15 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// Index of the calling wave inside its block, as a wave-uniform (scalar)
+// value.  MFMA instructions do not honour the EXEC mask, so every condition
+// that decides whether an MFMA runs must be a scalar branch; deriving it from
+// threadIdx.x directly would let the compiler lower it to EXEC masking.
+__device__ __forceinline__ int wave_id()
+{
+    return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
 // Blocks are dispatched round-robin over the 8 XCDs (block b runs on XCD
 // b % 8).  Renumber so that each XCD receives one contiguous range of
 // logical work items: neighbouring items (for example the column slabs of

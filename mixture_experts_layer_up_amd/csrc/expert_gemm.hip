@@ -12,314 +12,373 @@
 // the gate_up delta is not scaled by the routing weight).
 //
 // Design for gfx950:
-//  * One block = 4 waves = one (local expert, 64-column slab).  The packed
-//    weight layout makes every B fragment a contiguous 1 KiB block, loaded by
-//    one 16-byte load per lane directly into registers (no LDS round trip):
-//    the weight stream is the HBM-bound part of the layer.
-//  * The 4 waves split K; each keeps its own fp32 accumulators for all rows
-//    of the expert (up to 64 per pass) and the partial sums are reduced
-//    through LDS once per pass.  Rows beyond 64 take further passes.
-//  * The LoRA expand is folded into the same MFMA accumulation as extra K:
-//    row p contributes s[p] (rank r, zero-padded to rp) in the K block of its
-//    own adapter and zeros elsewhere, against B[l, e]^T, so
-//    acc = X W + sum_l S_l B_l^T with no separate delta buffer.  K chunks of
-//    adapters absent from the pass are skipped.
+//  * Work list: the permute kernel cuts every expert's rows into tiles of at
+//    most 16 * MT rows.  One block = 4 waves = one (tile, 64-column slab).
+//    Tiles of the same expert are numbered next to each other, so blocks that
+//    stream the same weight slab run at the same time on the same XCD and the
+//    slab comes from HBM once.
+//  * The packed weight layout makes every B fragment a contiguous 1 KiB
+//    block, loaded by one 16-byte load per lane straight into registers (no
+//    LDS): the weight stream is the HBM-bound part of the layer.
+//  * The 4 waves split K.  Each wave runs a two-stage software pipeline over
+//    its K chunks (the loads of stage s + 1 are in flight while stage s
+//    multiplies); the first stage's weight loads are issued before the row
+//    lookups, which are a chain of dependent loads.  Partial sums are reduced
+//    through LDS at the end.
+//  * The LoRA expand is folded into the same accumulation as extra K chunks
+//    at the end of each wave's sequence: row p contributes s[p] (rank r,
+//    zero-padded to rp) in the K block of its own adapter and zeros
+//    elsewhere, against B[l, e]^T, so acc = X W + sum_l S_l B_l^T and no
+//    delta buffer exists.
 //  * gate_up blocks own matching gate and up columns (packed tile order), so
 //    SwiGLU runs in the epilogue and h never reaches memory.
-//  * Blocks are renumbered so each XCD processes contiguous experts.
+//  * Every load in the pipeline is issued unconditionally (indices clamped,
+//    values masked afterwards) so all paths have the same number of
+//    outstanding loads and the compiler's wait counts stay exact.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace moe_lora {
 namespace {
 
-constexpr int kMT = 4;                 // M tiles (16 rows) per pass
-constexpr int kNS = 4;                 // 16-column N tiles per block
-constexpr int kRows = kMT * 16;        // rows per pass
-constexpr int kCH = 4;                 // K chunks (32) loaded per batch
-constexpr int kPartStride = kNS * 16 + 4;
-constexpr int kPartFloats = 4 * kRows * kPartStride;
+constexpr int kNS = 4;  // 16-column N tiles per block (64 columns)
 
-__device__ __forceinline__ void zero_acc(f32x4 (&acc)[kMT][kNS])
+template <int MT>
+struct Part {
+    static constexpr int kRows = MT * 16;
+    static constexpr int kStride = kNS * 16 + 4;
+    static constexpr int kWaveFloats = kRows * kStride;
+    static constexpr int kFloats = 4 * kWaveFloats;
+};
+
+template <int MT, int NS>
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[MT][NS])
 {
 #pragma unroll
-    for (int m = 0; m < kMT; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int n = 0; n < kNS; ++n)
+        for (int n = 0; n < NS; ++n)
             acc[m][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
-// Write this wave's accumulators as [row][col] fp32 partials.
-__device__ __forceinline__ void store_partials(float *part, const f32x4 (&acc)[kMT][kNS],
+// Write this wave's accumulators as [row][col] fp32 partials (col < 16 * NS).
+template <int MT, int NS>
+__device__ __forceinline__ void store_partials(float *part, const f32x4 (&acc)[MT][NS],
                                                int n_mt, int wave, int lane)
 {
-    float *pw = part + wave * kRows * kPartStride;
+    float *pw = part + wave * Part<MT>::kWaveFloats;
 #pragma unroll
-    for (int m = 0; m < kMT; ++m) {
+    for (int m = 0; m < MT; ++m) {
         if (m < n_mt) {
 #pragma unroll
-            for (int n = 0; n < kNS; ++n) {
+            for (int n = 0; n < NS; ++n) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    pw[(m * 16 + 4 * (lane >> 4) + i) * kPartStride + n * 16 + (lane & 15)] =
+                    pw[(m * 16 + 4 * (lane >> 4) + i) * Part<MT>::kStride + n * 16 + (lane & 15)] =
                         acc[m][n][i];
             }
         }
     }
 }
 
+template <int MT>
 __device__ __forceinline__ float sum_partials(const float *part, int row, int col)
 {
-    const int o = row * kPartStride + col;
-    return (part[o] + part[kRows * kPartStride + o]) +
-           (part[2 * kRows * kPartStride + o] + part[3 * kRows * kPartStride + o]);
+    constexpr int W = Part<MT>::kWaveFloats;
+    const int o = row * Part<MT>::kStride + col;
+    return (part[o] + part[W + o]) + (part[2 * W + o] + part[3 * W + o]);
 }
 
-// Accumulate this wave's share of the K chunks [kbeg, kend):
-// acc[m][n] += A rows (via aptr) x B tiles (via bptr).
-template <typename BLoad>
-__device__ __forceinline__ void k_loop(f32x4 (&acc)[kMT][kNS], const uint16_t *const (&aptr)[kMT],
-                                       const bool (&ok)[kMT], int n_mt, int kbeg, int kend,
-                                       BLoad bload)
+template <int MT, int NS, int CH>
+struct Stage {
+    u32x4 b[CH][NS];
+    u32x4 a[CH][MT];
+};
+
+// Two-stage pipeline over virtual chunks [0, nv).  load_b(vc, b[NS]) and
+// load_a(vc, a[MT]) fill one chunk's operands; s0.b may already hold the
+// first stage's B operands (b0_ready).
+template <int MT, int NS, int CH, typename LoadB, typename LoadA>
+__device__ __forceinline__ void run_pipeline(f32x4 (&acc)[MT][NS], int nv, int n_mt,
+                                             Stage<MT, NS, CH> &s0, Stage<MT, NS, CH> &s1,
+                                             bool b0_ready, LoadB load_b, LoadA load_a)
 {
-    for (int kc0 = kbeg; kc0 < kend; kc0 += kCH) {
-        u32x4 b[kCH][kNS];
-        u32x4 av[kCH][kMT];
+    if (nv <= 0)
+        return;
+    auto load_stage = [&](Stage<MT, NS, CH> &st, int vc0, bool with_b) {
 #pragma unroll
-        for (int c = 0; c < kCH; ++c) {
-            const int kc = kc0 + c;
-            if (kc < kend) {
-#pragma unroll
-                for (int n = 0; n < kNS; ++n)
-                    b[c][n] = bload(n, kc);
-#pragma unroll
-                for (int m = 0; m < kMT; ++m)
-                    av[c][m] = ok[m] ? load16(aptr[m] + kc * 32) : zero16();
-            }
+        for (int c = 0; c < CH; ++c) {
+            const int vc = min(vc0 + c, nv - 1);
+            if (with_b)
+                load_b(vc, st.b[c]);
+            load_a(vc, st.a[c]);
         }
+    };
+    auto compute_stage = [&](const Stage<MT, NS, CH> &st, int vc0) {
 #pragma unroll
-        for (int c = 0; c < kCH; ++c) {
-            if (kc0 + c < kend) {
+        for (int c = 0; c < CH; ++c) {
+            if (vc0 + c < nv) {
 #pragma unroll
-                for (int m = 0; m < kMT; ++m) {
+                for (int m = 0; m < MT; ++m) {
                     if (m < n_mt) {
 #pragma unroll
-                        for (int n = 0; n < kNS; ++n)
-                            acc[m][n] = mfma_16x16x32(av[c][m], b[c][n], acc[m][n]);
+                        for (int n = 0; n < NS; ++n)
+                            acc[m][n] = mfma_16x16x32(st.a[c][m], st.b[c][n], acc[m][n]);
                     }
                 }
             }
         }
+    };
+    load_stage(s0, 0, !b0_ready);
+    int vc0 = 0;
+    while (true) {
+        const int v1 = vc0 + CH;
+        if (v1 < nv)
+            load_stage(s1, v1, true);
+        compute_stage(s0, vc0);
+        if (v1 >= nv)
+            break;
+        const int v2 = v1 + CH;
+        if (v2 < nv)
+            load_stage(s0, v2, true);
+        compute_stage(s1, v1);
+        if (v2 >= nv)
+            break;
+        vc0 = v2;
     }
 }
 
-template <bool kGated>
-__global__ __launch_bounds__(256) void expert_gemm_kernel(GemmArgs a)
+template <int MT, int CH, bool kGated>
+__global__ __launch_bounds__(256, MT == 1 ? 2 : 1) void expert_gemm_kernel(GemmArgs a)
 {
-    __shared__ float part[kPartFloats];
+    constexpr int NS = kNS;
+    __shared__ float part[Part<MT>::kFloats];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid >> 6;
+    const int wave = wave_id();
 
     const int logical = xcd_contiguous_index(blockIdx.x, gridDim.x);
-    const int le = logical / a.n_slabs;
-    const int slab = logical - le * a.n_slabs;
-    const int row0 = a.offsets[le];
-    const int n_rows = a.offsets[le + 1] - row0;
-    if (n_rows <= 0)
+    const int tile = logical / a.n_slabs;
+    const int slab = logical - tile * a.n_slabs;
+    const int4 te = a.tiles[tile];
+    const int le = te.x;
+    if (le < 0)
         return;
+    const int row0 = te.y;
+    const int n_rows = te.z;  // 1 .. 16 * MT
+    const int n_mt = (n_rows + 15) >> 4;
 
     const int KC = a.K >> 5;
     const int kc_per = (KC + 3) >> 2;
     const int kbeg = min(KC, wave * kc_per);
-    const int kend = min(KC, kbeg + kc_per);
+    const int nm = min(KC, kbeg + kc_per) - kbeg;  // this wave's main chunks
     const bool lora = a.S != nullptr && a.L > 0 && a.r > 0;
     const int n_ext = lora ? (a.L * a.rp + 31) >> 5 : 0;
+    const int ne = wave < n_ext ? (n_ext - wave + 3) >> 2 : 0;  // ext chunks wave, wave+4, ..
+    const int nv = nm + ne;
 
-    // B fragments of this block's 4 packed tiles: tile n, chunk kc at
-    // wbase + (n * KC + kc) * 512 elements.
     const uint16_t *wbase =
-        a.Wp + ((size_t)le * a.NT + (size_t)slab * kNS) * (size_t)KC * 512 + lane * 8;
-    auto bload = [&](int n, int kc) { return load16(wbase + ((size_t)n * KC + kc) * 512); };
-
-    for (int pass = 0; pass < n_rows; pass += kRows) {
-        const int rows = min(kRows, n_rows - pass);
-        const int n_mt = (rows + 15) >> 4;
-
-        const uint16_t *aptr[kMT];
-        bool ok[kMT];
-        int prow[kMT];
-        int adapter[kMT];
+        a.Wp + ((size_t)le * a.NT + (size_t)slab * NS) * (size_t)KC * 512 + lane * 8;
+    auto load_b = [&](int vc, u32x4 (&b)[NS]) {
+        if (vc < nm) {
+            const int kc = kbeg + vc;
 #pragma unroll
-        for (int m = 0; m < kMT; ++m) {
-            const int r = pass + m * 16 + (lane & 15);
-            ok[m] = r < n_rows;
-            const int p = row0 + min(r, n_rows - 1);
-            prow[m] = p;
-            const int tok = a.perm2exp[p] / a.k;
-            aptr[m] = a.X + (size_t)(a.gather_by_token ? tok : p) * a.K + (lane >> 4) * 8;
-            const int l = (lora && a.mapping) ? a.mapping[tok] : -1;
-            adapter[m] = (l >= 0 && l < a.L) ? l : -1;
-        }
-
-        f32x4 acc[kMT][kNS];
-        zero_acc(acc);
-        k_loop(acc, aptr, ok, n_mt, kbeg, kend, bload);
-
-        if (n_ext > 0) {
-            unsigned long long present = 0;
-            for (int l = 0; l < a.L; ++l) {
-                bool has = false;
+            for (int n = 0; n < NS; ++n)
+                b[n] = load16(wbase + ((size_t)n * KC + kc) * 512);
+        } else {
+            const int c = (vc - nm) * 4 + wave;
+            const int g = c * 32 + (lane >> 4) * 8;
+            const int aid = g / a.rp;
+            const int q0 = g - aid * a.rp;
+            const int aid_c = min(aid, a.L - 1);
 #pragma unroll
-                for (int m = 0; m < kMT; ++m)
-                    has |= ok[m] && adapter[m] == l;
-                if (__ballot(has))
-                    present |= 1ull << l;
-            }
-            for (int c = wave; c < n_ext; c += 4) {
-                const int lo = (c * 32) / a.rp;
-                const int hi = min(a.L - 1, (c * 32 + 31) / a.rp);
-                const int span = hi - lo + 1;
-                const unsigned long long mask = span >= 64 ? ~0ull : ((1ull << span) - 1ull);
-                if (((present >> lo) & mask) == 0)
-                    continue;
-                const int g = c * 32 + (lane >> 4) * 8;
-                const int aid = g / a.rp;
-                const int q0 = g - aid * a.rp;
-                u32x4 av[kMT];
-                u32x4 b[kNS];
+            for (int n = 0; n < NS; ++n) {
+                const int col = kGated ? (n & 1) * a.I + (slab * 2 + (n >> 1)) * 16 + (lane & 15)
+                                       : (slab * NS + n) * 16 + (lane & 15);
+                const uint16_t *src =
+                    a.LB + (((size_t)aid_c * a.E_l + le) * a.n_canon + col) * a.r;
+                u32x4 v;
+                if ((a.r & 7) == 0) {
+                    v = load16(src + q0);
+                } else {
+                    uint32_t w[4];
 #pragma unroll
-                for (int m = 0; m < kMT; ++m)
-                    av[m] = (ok[m] && adapter[m] == aid)
-                                ? load16(a.S + (size_t)prow[m] * a.rp + q0)
-                                : zero16();
-#pragma unroll
-                for (int n = 0; n < kNS; ++n) {
-                    b[n] = zero16();
-                    if (aid < a.L) {
-                        const int col = kGated
-                                            ? (n & 1) * a.I + (slab * 2 + (n >> 1)) * 16 + (lane & 15)
-                                            : (slab * kNS + n) * 16 + (lane & 15);
-                        const uint16_t *src =
-                            a.LB + (((size_t)aid * a.E_l + le) * a.n_canon + col) * a.r + q0;
-                        if ((a.r & 7) == 0) {
-                            b[n] = load16(src);
-                        } else {
-                            uint32_t w[4] = {0u, 0u, 0u, 0u};
-                            for (int i = 0; i < 8; ++i)
-                                if (q0 + i < a.r)
-                                    w[i >> 1] |= (uint32_t)src[i] << (16 * (i & 1));
-                            b[n] = u32x4{w[0], w[1], w[2], w[3]};
-                        }
+                    for (int i = 0; i < 8; i += 2) {
+                        const uint32_t lo = src[min(q0 + i, a.r - 1)];
+                        const uint32_t hi = src[min(q0 + i + 1, a.r - 1)];
+                        w[i >> 1] = (q0 + i < a.r ? lo : 0u) | ((q0 + i + 1 < a.r ? hi : 0u) << 16);
                     }
+                    v = u32x4{w[0], w[1], w[2], w[3]};
                 }
-#pragma unroll
-                for (int m = 0; m < kMT; ++m) {
-                    if (m < n_mt) {
-#pragma unroll
-                        for (int n = 0; n < kNS; ++n)
-                            acc[m][n] = mfma_16x16x32(av[m], b[n], acc[m][n]);
-                    }
-                }
+                b[n] = aid < a.L ? v : zero16();
             }
         }
+    };
 
-        __syncthreads();  // the previous pass's epilogue is done with `part`
-        store_partials(part, acc, n_mt, wave, lane);
-        __syncthreads();
+    Stage<MT, NS, CH> s0, s1;
+    const bool early = nm >= CH;
+    if (early) {  // weight loads of stage 0 do not depend on the rows
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+            load_b(c, s0.b[c]);
+    }
 
-        if (kGated) {
-            // 32 activation columns per row: 4 groups of 8 (pair jj, half c0)
-            for (int item = tid; item < rows * 4; item += 256) {
-                const int row = item >> 2;
-                const int jj = (item >> 1) & 1;
-                const int c0 = (item & 1) * 8;
-                uint32_t packed[4];
+    // rows of this tile; lanes past the tile's rows read a clamped valid row
+    const uint16_t *aptr[MT];
+    bool ok[MT];
+    int prow[MT];
+    int adapter[MT];
 #pragma unroll
-                for (int i = 0; i < 8; i += 2) {
-                    float v[2];
+    for (int m = 0; m < MT; ++m) {
+        const int r = m * 16 + (lane & 15);
+        ok[m] = r < n_rows;
+        const int p = row0 + min(r, n_rows - 1);
+        prow[m] = p;
+        const int tok = a.perm2exp[p] / a.k;
+        aptr[m] = a.X + (size_t)(a.gather_by_token ? tok : p) * a.K + (lane >> 4) * 8;
+        const int l = (lora && a.mapping) ? a.mapping[tok] : -1;
+        adapter[m] = (l >= 0 && l < a.L) ? l : -1;
+    }
+    auto load_a = [&](int vc, u32x4 (&av)[MT]) {
+        if (vc < nm) {
+            const int kc = kbeg + vc;
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const float gate = sum_partials(part, row, (2 * jj) * 16 + c0 + i + h);
-                        const float up = sum_partials(part, row, (2 * jj + 1) * 16 + c0 + i + h);
-                        v[h] = silu_f32(gate) * up;
-                    }
-                    packed[i >> 1] = float_to_bf16_bits(v[0]) | (float_to_bf16_bits(v[1]) << 16);
+            for (int m = 0; m < MT; ++m) {
+                if (m < n_mt) {
+                    const u32x4 v = load16(aptr[m] + kc * 32);
+                    av[m] = ok[m] ? v : zero16();
                 }
-                const int p = row0 + pass + row;
-                store16(a.Y + (size_t)p * a.I + (slab * 2 + jj) * 16 + c0,
-                        u32x4{packed[0], packed[1], packed[2], packed[3]});
             }
         } else {
-            // 64 output columns per row: 8 groups of 8
-            for (int item = tid; item < rows * 8; item += 256) {
-                const int row = item >> 3;
-                const int c0 = (item & 7) * 8;
-                uint32_t packed[4];
+            const int c = (vc - nm) * 4 + wave;
+            const int g = c * 32 + (lane >> 4) * 8;
+            const int aid = g / a.rp;
+            const int q0 = g - aid * a.rp;
 #pragma unroll
-                for (int i = 0; i < 8; i += 2) {
-                    const float v0 = sum_partials(part, row, c0 + i);
-                    const float v1 = sum_partials(part, row, c0 + i + 1);
-                    packed[i >> 1] = float_to_bf16_bits(v0) | (float_to_bf16_bits(v1) << 16);
+            for (int m = 0; m < MT; ++m) {
+                if (m < n_mt) {
+                    const u32x4 v = load16(a.S + (size_t)prow[m] * a.rp + q0);
+                    av[m] = (ok[m] && adapter[m] == aid) ? v : zero16();
                 }
-                const int p = row0 + pass + row;
-                store16(a.Y + (size_t)p * a.n_canon + slab * 64 + c0,
-                        u32x4{packed[0], packed[1], packed[2], packed[3]});
             }
+        }
+    };
+
+    f32x4 acc[MT][NS];
+    zero_acc(acc);
+    run_pipeline<MT, NS, CH>(acc, nv, n_mt, s0, s1, early, load_b, load_a);
+
+    store_partials<MT, NS>(part, acc, n_mt, wave, lane);
+    __syncthreads();
+
+    if (kGated) {
+        // 32 activation columns per row: 4 groups of 8 (gate/up pair jj, half c0)
+        for (int item = tid; item < n_rows * 4; item += 256) {
+            const int row = item >> 2;
+            const int jj = (item >> 1) & 1;
+            const int c0 = (item & 1) * 8;
+            uint32_t packed[4];
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+                float v[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float gate = sum_partials<MT>(part, row, (2 * jj) * 16 + c0 + i + h);
+                    const float up = sum_partials<MT>(part, row, (2 * jj + 1) * 16 + c0 + i + h);
+                    v[h] = silu_f32(gate) * up;
+                }
+                packed[i >> 1] = float_to_bf16_bits(v[0]) | (float_to_bf16_bits(v[1]) << 16);
+            }
+            store16(a.Y + (size_t)(row0 + row) * a.I + (slab * 2 + jj) * 16 + c0,
+                    u32x4{packed[0], packed[1], packed[2], packed[3]});
+        }
+    } else {
+        // 64 output columns per row: 8 groups of 8
+        for (int item = tid; item < n_rows * 8; item += 256) {
+            const int row = item >> 3;
+            const int c0 = (item & 7) * 8;
+            uint32_t packed[4];
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+                const float v0 = sum_partials<MT>(part, row, c0 + i);
+                const float v1 = sum_partials<MT>(part, row, c0 + i + 1);
+                packed[i >> 1] = float_to_bf16_bits(v0) | (float_to_bf16_bits(v1) << 16);
+            }
+            store16(a.Y + (size_t)(row0 + row) * a.n_canon + slab * 64 + c0,
+                    u32x4{packed[0], packed[1], packed[2], packed[3]});
         }
     }
 }
 
 // LoRA shrink: S[p, 0:rp] = A[l, e] x_p for the slots of one virtual expert
-// (adapter l, local expert e) per block; q >= r is written as 0.  The LoRA A
-// stack [r, K] is K-contiguous, which is exactly the per-lane B operand
-// layout of the MFMA (8 consecutive K values of one column q).
-__global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a)
+// (adapter l, local expert e) per block, 16 rows per pass; q >= r is written
+// as 0.  The stack A[l, e] (r x K) is K-contiguous per rank row, which is
+// exactly the per-lane B operand layout of the MFMA (8 consecutive K values of
+// one column q).  NS 16-column tiles of q per pass over N.
+template <int NS, int CH>
+__global__ __launch_bounds__(256, 2) void lora_shrink_kernel(ShrinkArgs a)
 {
-    __shared__ float part[kPartFloats];
+    constexpr int MT = 1;
+    __shared__ float part[Part<MT>::kFloats];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid >> 6;
+    const int wave = wave_id();
     const int seg = blockIdx.x;  // = l * E_l + e, the stack's own order
+    const int KC = a.K >> 5;
+    const int kc_per = (KC + 3) >> 2;
+    const int kbeg = min(KC, wave * kc_per);
+    const int nm = min(KC, kbeg + kc_per) - kbeg;
+    const int n_nt = (a.r + 15) >> 4;
+    const uint16_t *abase = a.A + (size_t)seg * a.r * a.K + (lane >> 4) * 8;
+
+    Stage<MT, NS, CH> s0, s1;
+    auto load_b_nt = [&](int nt0, int vc, u32x4 (&b)[NS]) {
+        const int kc = kbeg + vc;
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            const int q = (nt0 + n) * 16 + (lane & 15);
+            const u32x4 v = load16(abase + (size_t)min(q, a.r - 1) * a.K + kc * 32);
+            b[n] = q < a.r ? v : zero16();
+        }
+    };
     const int beg = a.seg_offsets[seg];
     const int n_rows = a.seg_offsets[seg + 1] - beg;
     if (n_rows <= 0)
         return;
-
-    const int KC = a.K >> 5;
-    const int kc_per = (KC + 3) >> 2;
-    const int kbeg = min(KC, wave * kc_per);
-    const int kend = min(KC, kbeg + kc_per);
-    const int n_nt = (a.r + 15) >> 4;
-    const uint16_t *abase = a.A + (size_t)seg * a.r * a.K + (lane >> 4) * 8;
-
-    for (int pass = 0; pass < n_rows; pass += kRows) {
-        const int rows = min(kRows, n_rows - pass);
-        const int n_mt = (rows + 15) >> 4;
-        const uint16_t *aptr[kMT];
-        bool ok[kMT];
+    // the stack's first stage does not depend on the rows: issue it before
+    // the dependent row lookups
+    const bool early = nm >= CH;
+    if (early) {
 #pragma unroll
-        for (int m = 0; m < kMT; ++m) {
-            const int r = pass + m * 16 + (lane & 15);
-            ok[m] = r < n_rows;
-            const int x = a.seg_slots[beg + min(r, n_rows - 1)];
-            const int p = a.exp2perm[x];
-            aptr[m] = a.X + (size_t)(a.gather_by_token ? x / a.k : p) * a.K + (lane >> 4) * 8;
-        }
-        for (int nt0 = 0; nt0 < n_nt; nt0 += kNS) {
-            auto bload = [&](int n, int kc) {
-                const int q = (nt0 + n) * 16 + (lane & 15);
-                return q < a.r ? load16(abase + (size_t)q * a.K + kc * 32) : zero16();
-            };
-            f32x4 acc[kMT][kNS];
+        for (int c = 0; c < CH; ++c)
+            load_b_nt(0, c, s0.b[c]);
+    }
+
+    bool first = true;
+    for (int pass = 0; pass < n_rows; pass += 16) {
+        const int rows = min(16, n_rows - pass);
+        const int r = pass + (lane & 15);
+        const bool ok = r < n_rows;
+        const int x = a.seg_slots[beg + min(r, n_rows - 1)];
+        const int p = a.exp2perm[x];
+        const uint16_t *aptr =
+            a.X + (size_t)(a.gather_by_token ? x / a.k : p) * a.K + (lane >> 4) * 8;
+        auto load_a = [&](int vc, u32x4 (&av)[MT]) {
+            const u32x4 v = load16(aptr + (kbeg + vc) * 32);
+            av[0] = ok ? v : zero16();
+        };
+        for (int nt0 = 0; nt0 < n_nt; nt0 += NS) {
+            auto load_b = [&](int vc, u32x4 (&b)[NS]) { load_b_nt(nt0, vc, b); };
+            f32x4 acc[MT][NS];
             zero_acc(acc);
-            k_loop(acc, aptr, ok, n_mt, kbeg, kend, bload);
+            run_pipeline<MT, NS, CH>(acc, nm, 1, s0, s1, first && early, load_b, load_a);
+            first = false;
 
-            __syncthreads();
-            store_partials(part, acc, n_mt, wave, lane);
+            __syncthreads();  // the previous epilogue is done with `part`
+            store_partials<MT, NS>(part, acc, 1, wave, lane);
             __syncthreads();
 
-            const int groups = min(kNS, n_nt - nt0) * 2;  // 8-wide q groups in this tile range
+            const int groups = min(NS, n_nt - nt0) * 2;  // 8-wide q groups
             for (int item = tid; item < rows * groups; item += 256) {
                 const int row = item / groups;
                 const int g = item - row * groups;
@@ -329,36 +388,48 @@ __global__ __launch_bounds__(256) void lora_shrink_kernel(ShrinkArgs a)
                 uint32_t packed[4];
 #pragma unroll
                 for (int i = 0; i < 8; i += 2) {
-                    const float v0 = (q0 + i < a.r) ? sum_partials(part, row, g * 8 + i) : 0.0f;
-                    const float v1 = (q0 + i + 1 < a.r) ? sum_partials(part, row, g * 8 + i + 1) : 0.0f;
+                    const float v0 = (q0 + i < a.r) ? sum_partials<MT>(part, row, g * 8 + i) : 0.0f;
+                    const float v1 =
+                        (q0 + i + 1 < a.r) ? sum_partials<MT>(part, row, g * 8 + i + 1) : 0.0f;
                     packed[i >> 1] = float_to_bf16_bits(v0) | (float_to_bf16_bits(v1) << 16);
                 }
-                const int x = a.seg_slots[beg + pass + row];
-                const int p = a.exp2perm[x];
-                store16(a.S + (size_t)p * a.rp + q0, u32x4{packed[0], packed[1], packed[2], packed[3]});
+                const int xo = a.seg_slots[beg + pass + row];
+                const int po = a.exp2perm[xo];
+                store16(a.S + (size_t)po * a.rp + q0, u32x4{packed[0], packed[1], packed[2], packed[3]});
             }
         }
     }
 }
 
+template <int MT, int CH, bool kGated>
+hipError_t launch_gemm_variant(const GemmArgs &a, hipStream_t s)
+{
+    const int blocks = a.n_tiles * a.n_slabs;
+    if (blocks <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((expert_gemm_kernel<MT, CH, kGated>), dim3(blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 } // namespace
+
+int gemm_tile_rows(int n_slots, int E_l)
+{
+    // rows per tile: 16 for decode-like batches (few rows per expert), 64
+    // when experts carry many rows (fewer re-reads of each weight slab)
+    return n_slots >= 32 * E_l ? 64 : 16;
+}
 
 hipError_t launch_gemm_gate_up(const GemmArgs &a, hipStream_t s)
 {
-    const int blocks = a.E_l * a.n_slabs;
-    if (blocks <= 0)
-        return hipSuccess;
-    hipLaunchKernelGGL((expert_gemm_kernel<true>), dim3(blocks), dim3(256), 0, s, a);
-    return hipGetLastError();
+    return a.tile_rows == 16 ? launch_gemm_variant<1, 2, true>(a, s)
+                             : launch_gemm_variant<4, 2, true>(a, s);
 }
 
 hipError_t launch_gemm_down(const GemmArgs &a, hipStream_t s)
 {
-    const int blocks = a.E_l * a.n_slabs;
-    if (blocks <= 0)
-        return hipSuccess;
-    hipLaunchKernelGGL((expert_gemm_kernel<false>), dim3(blocks), dim3(256), 0, s, a);
-    return hipGetLastError();
+    return a.tile_rows == 16 ? launch_gemm_variant<1, 2, false>(a, s)
+                             : launch_gemm_variant<4, 2, false>(a, s);
 }
 
 hipError_t launch_shrink(const ShrinkArgs &a, hipStream_t s)
@@ -366,7 +437,10 @@ hipError_t launch_shrink(const ShrinkArgs &a, hipStream_t s)
     const int blocks = a.L * a.E_l;
     if (blocks <= 0 || a.r <= 0)
         return hipSuccess;
-    hipLaunchKernelGGL(lora_shrink_kernel, dim3(blocks), dim3(256), 0, s, a);
+    if (a.r <= 16)
+        hipLaunchKernelGGL((lora_shrink_kernel<1, 8>), dim3(blocks), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((lora_shrink_kernel<4, 2>), dim3(blocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

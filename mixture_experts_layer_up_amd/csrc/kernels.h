@@ -21,7 +21,18 @@ struct PermuteArgs {
     int32_t *expert_counts, *expert_offsets;
     int32_t *exp2perm, *perm2exp;
     int32_t *seg_offsets, *seg_slots;
+    // GEMM work list (optional): one int4 {local expert, first permuted row,
+    // rows, 0} per chunk of at most tile_rows rows of one expert; unused
+    // entries up to max_tiles have expert -1.
+    int4 *tiles;
+    int tile_rows, max_tiles;
 };
+
+// Upper bound on the GEMM work-list length for n slots and E_l experts.
+inline int max_gemm_tiles(int n, int E_l, int tile_rows)
+{
+    return (n + tile_rows - 1) / tile_rows + (E_l < n ? E_l : n);
+}
 
 struct PackArgs {
     const uint16_t *src;   // [E_l, K, N]
@@ -52,12 +63,16 @@ struct GemmArgs {
     const uint16_t *LB;       // [L, E_l, n_canon, r] or null
     int r, rp, L, n_canon;
     const int32_t *mapping;   // [T] or null
-    const int32_t *offsets;   // [E_l + 1]
+    const int4 *tiles;        // work list written by the permute kernel
+    int n_tiles, tile_rows;   // list length (upper bound), rows per tile
     const int32_t *perm2exp;  // [n]
     int E_l, k, I;
     uint16_t *Y;              // gated: act [n, I]; else y [n, n_canon]
     int n_slabs;
 };
+
+// Rows per GEMM work-list tile for n local slots over E_l experts (16 or 64).
+int gemm_tile_rows(int n_slots, int E_l);
 
 struct FinalizeArgs {
     const uint16_t *Y;        // [n, H]

@@ -45,6 +45,8 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a)
     __shared__ int hist[kMaxKeys + 1];
     __shared__ int table[kTable];
     __shared__ int wave_excl[kWaves];
+    __shared__ int tile_excl[kWaves];
+    __shared__ int tile_total;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -123,6 +125,51 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a)
     const int total = hist[NK];
     for (int i = total + tid; i < n; i += kThreads)
         out_list[i] = -1;
+
+    // GEMM work list: chunks of at most tile_rows rows per expert, in expert
+    // order.  Same run-per-thread scan as above, over ceil(count / tile_rows).
+    if (!by_segment && a.tiles) {
+        int tl = 0;
+        for (int i = beg; i < end; ++i) {
+            const int c = (i + 1 < NK ? hist[i + 1] : total) - hist[i];
+            tl += (c + a.tile_rows - 1) / a.tile_rows;
+        }
+        int ti = tl;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int o = __shfl_up(ti, off);
+            if (lane >= off)
+                ti += o;
+        }
+        if (lane == kWave - 1)
+            tile_excl[wave] = ti;
+        __syncthreads();
+        if (wave == 0) {
+            const int ws = lane < kWaves ? tile_excl[lane] : 0;
+            int wi = ws;
+#pragma unroll
+            for (int off = 1; off < kWaves; off <<= 1) {
+                const int o = __shfl_up(wi, off);
+                if (lane >= off)
+                    wi += o;
+            }
+            if (lane < kWaves)
+                tile_excl[lane] = wi - ws;
+        }
+        __syncthreads();
+        int t0 = tile_excl[wave] + ti - tl;
+        for (int i = beg; i < end; ++i) {
+            const int first = hist[i];
+            const int c = (i + 1 < NK ? hist[i + 1] : total) - first;
+            for (int r = 0; r < c; r += a.tile_rows)
+                a.tiles[t0++] = make_int4(i, first + r, min(a.tile_rows, c - r), 0);
+        }
+        if (tid == kThreads - 1)  // t0 is now the number of tiles
+            tile_total = t0;
+        __syncthreads();
+        for (int i = tile_total + tid; i < a.max_tiles; i += kThreads)
+            a.tiles[i] = make_int4(-1, 0, 0, 0);
+    }
 
     // 3. stable ranks: split the slots into W contiguous chunks, one per wave
     const int W = max(1, min(kWaves, kTable / NK));

@@ -158,6 +158,8 @@ def main():
     ap.add_argument("--workload", default="decode64", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle baseline time budget (0 = skip)")
+    ap.add_argument("--graph-steps", type=int, default=200,
+                    help="also time this many steps replayed from a captured HIP graph (0 = skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain copy kernel (torch.neg) over this many MiB, "
                          "to calibrate HBM byte counters against a known size")
@@ -227,6 +229,34 @@ def main():
         hip.destroy(e)
     hip.destroy([start, end])
 
+    # the same step replayed from a HIP graph (the forward allocates nothing and
+    # never waits on the host, so it captures as-is); reported next to `value`
+    graph_ms = None
+    if args.graph_steps > 0:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(5):
+            g.replay()
+        torch.cuda.synchronize()
+        gs, ge = hip.create(2)
+        stream = torch.cuda.current_stream().cuda_stream
+        hip.record(gs, stream)
+        for _ in range(args.graph_steps):
+            g.replay()
+        hip.record(ge, stream)
+        hip.sync(ge)
+        graph_ms = hip.elapsed_ms(gs, ge) / args.graph_steps
+        hip.destroy([gs, ge])
+        del g
+        log(f"[bench] graph replay: {graph_ms * 1e3:.1f} us/step")
+
     # the cost model counts what this batch's routing touches (the library's own routing)
     routing = binding.alloc_routing(shape, "cuda")
     binding.forward(shape, lay["hidden"], lay["w13_packed"], lay["w2_packed"], out=out,
@@ -274,6 +304,9 @@ def main():
                   "local_slots": cost["local_slots"]},
         "stages_us": {n: float(v * 1e3) for n, v in zip(binding.STAGE_NAMES, stage_ms)},
         "wall_ms_per_step": wall_s * 1e3 / K,
+        "graph_replay": None if graph_ms is None else {
+            "ms_per_step": graph_ms, "tokens_per_s": cfg.num_tokens / (graph_ms / 1e3),
+            "layer_hbm_frac": cost["bytes"] / (graph_ms / 1e3) / 1e9 / HBM_PEAK_GBPS},
         "cpu_baseline": cpu,
     }
     print(json.dumps(result))

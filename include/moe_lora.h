@@ -166,13 +166,14 @@ size_t moe_lora_packed_w2_bytes(const moe_lora_shape *shape);
  * once at load: "BF16 support for the experimental_sgl_trtllm MoE-LoRA path",
  * Summary and "Files changed" table, base_backend row).
  *   w13 bf16 [E_l, H, 2I] -> w13_packed, w2 bf16 [E_l, I, H] -> w2_packed.
- * Packed layout: for expert e, column tile n (16 columns), K chunk c (32
- * rows), lane l (0..63), element i (0..7), the bf16 at
- *   ((e * NT + n) * KC + c) * 512 + l * 8 + i
- * is W[e][32c + 8(l / 16) + i][col(n) + l % 16], with NT = N / 16, KC = K/32.
- * For w13, col(n) = (n % 2) * I + (n / 2) * 16 (gate and up tiles of the same
- * columns alternate); for w2, col(n) = 16 n.  All four pointers 16-byte
- * aligned; outputs must not overlap inputs.
+ * Packed layout: for expert e, 64-column slab s, K chunk c (32 rows), tile t
+ * (0..3, 16 columns), lane l (0..63), element i (0..7), the bf16 at
+ *   (((e * NS + s) * KC + c) * 4 + t) * 512 + l * 8 + i
+ * is W[e][32c + 8(l / 16) + i][col(4s + t) + l % 16], with NS = N / 64 slabs
+ * and KC = K / 32 chunks.  For w13 (N = 2I), col(n) = (n % 2) * I + (n / 2) * 16
+ * (gate and up tiles of the same columns alternate); for w2 (N = H),
+ * col(n) = 16 n.  All four pointers 16-byte aligned; outputs must not overlap
+ * inputs.
  */
 int moe_lora_pack_weights(const moe_lora_shape *shape, const void *w13, const void *w2,
                           void *w13_packed, void *w2_packed, void *stream);

@@ -30,6 +30,14 @@ __device__ __forceinline__ u32x4 load16(const void *p)
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// Streaming load for data read once per call (expert weights, LoRA stacks):
+// the nontemporal hint keeps it from displacing reused lines in the caches
+// and lets the memory system stream it at a higher rate.
+__device__ __forceinline__ u32x4 load16_stream(const void *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
 __device__ __forceinline__ void store16(void *p, u32x4 v)
 {
     *reinterpret_cast<u32x4 *>(p) = v;

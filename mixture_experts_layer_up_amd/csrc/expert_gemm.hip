@@ -168,23 +168,24 @@ __global__ __launch_bounds__(256, MT == 1 ? 2 : 1) void expert_gemm_kernel(GemmA
     const int n_rows = te.z;  // 1 .. 16 * MT
     const int n_mt = (n_rows + 15) >> 4;
 
+    // waves take K chunks round-robin (wave w: chunks w, w + 4, ...), so the
+    // block's loads at any moment cover one contiguous stretch of its slab
     const int KC = a.K >> 5;
-    const int kc_per = (KC + 3) >> 2;
-    const int kbeg = min(KC, wave * kc_per);
-    const int nm = min(KC, kbeg + kc_per) - kbeg;  // this wave's main chunks
+    const int nm = wave < KC ? (KC - wave + 3) >> 2 : 0;  // this wave's main chunks
     const bool lora = a.S != nullptr && a.L > 0 && a.r > 0;
     const int n_ext = lora ? (a.L * a.rp + 31) >> 5 : 0;
     const int ne = wave < n_ext ? (n_ext - wave + 3) >> 2 : 0;  // ext chunks wave, wave+4, ..
     const int nv = nm + ne;
 
+    // this block's slab: KC chunks of NS consecutive 1 KiB fragments
     const uint16_t *wbase =
-        a.Wp + ((size_t)le * a.NT + (size_t)slab * NS) * (size_t)KC * 512 + lane * 8;
+        a.Wp + ((size_t)le * a.n_slabs + slab) * (size_t)KC * NS * 512 + lane * 8;
     auto load_b = [&](int vc, u32x4 (&b)[NS]) {
         if (vc < nm) {
-            const int kc = kbeg + vc;
+            const int kc = wave + 4 * vc;
 #pragma unroll
             for (int n = 0; n < NS; ++n)
-                b[n] = load16(wbase + ((size_t)n * KC + kc) * 512);
+                b[n] = load16_stream(wbase + ((size_t)kc * NS + n) * 512);
         } else {
             const int c = (vc - nm) * 4 + wave;
             const int g = c * 32 + (lane >> 4) * 8;
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(256, MT == 1 ? 2 : 1) void expert_gemm_kernel(GemmA
                     a.LB + (((size_t)aid_c * a.E_l + le) * a.n_canon + col) * a.r;
                 u32x4 v;
                 if ((a.r & 7) == 0) {
-                    v = load16(src + q0);
+                    v = load16_stream(src + q0);
                 } else {
                     uint32_t w[4];
 #pragma unroll
@@ -226,22 +227,23 @@ __global__ __launch_bounds__(256, MT == 1 ? 2 : 1) void expert_gemm_kernel(GemmA
     // rows of this tile; lanes past the tile's rows read a clamped valid row
     const uint16_t *aptr[MT];
     bool ok[MT];
-    int prow[MT];
+    int xslot[MT];
     int adapter[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
         const int r = m * 16 + (lane & 15);
         ok[m] = r < n_rows;
         const int p = row0 + min(r, n_rows - 1);
-        prow[m] = p;
-        const int tok = a.perm2exp[p] / a.k;
+        const int x = a.perm2exp[p];
+        xslot[m] = x;
+        const int tok = x / a.k;
         aptr[m] = a.X + (size_t)(a.gather_by_token ? tok : p) * a.K + (lane >> 4) * 8;
         const int l = (lora && a.mapping) ? a.mapping[tok] : -1;
         adapter[m] = (l >= 0 && l < a.L) ? l : -1;
     }
     auto load_a = [&](int vc, u32x4 (&av)[MT]) {
         if (vc < nm) {
-            const int kc = kbeg + vc;
+            const int kc = wave + 4 * vc;
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 if (m < n_mt) {
@@ -257,7 +259,7 @@ __global__ __launch_bounds__(256, MT == 1 ? 2 : 1) void expert_gemm_kernel(GemmA
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 if (m < n_mt) {
-                    const u32x4 v = load16(a.S + (size_t)prow[m] * a.rp + q0);
+                    const u32x4 v = load16(a.S + (size_t)xslot[m] * a.rp + q0);
                     av[m] = (ok[m] && adapter[m] == aid) ? v : zero16();
                 }
             }
@@ -310,9 +312,10 @@ __global__ __launch_bounds__(256, MT == 1 ? 2 : 1) void expert_gemm_kernel(GemmA
     }
 }
 
-// LoRA shrink: S[p, 0:rp] = A[l, e] x_p for the slots of one virtual expert
-// (adapter l, local expert e) per block, 16 rows per pass; q >= r is written
-// as 0.  The stack A[l, e] (r x K) is K-contiguous per rank row, which is
+// LoRA shrink: S[x, 0:rp] = A[l, e] x_row for the slots x of one virtual
+// expert (adapter l, local expert e) per block, 16 rows per pass; q >= r is
+// written as 0.  S is indexed by slot, so the gate_up shrink (rows = the
+// slots' tokens) needs no permutation lookup at all.  The stack A[l, e] (r x K) is K-contiguous per rank row, which is
 // exactly the per-lane B operand layout of the MFMA (8 consecutive K values of
 // one column q).  NS 16-column tiles of q per pass over N.
 template <int NS, int CH>
@@ -320,6 +323,7 @@ __global__ __launch_bounds__(256, 2) void lora_shrink_kernel(ShrinkArgs a)
 {
     constexpr int MT = 1;
     __shared__ float part[Part<MT>::kFloats];
+    __shared__ int row_slot[16];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = wave_id();
@@ -337,7 +341,7 @@ __global__ __launch_bounds__(256, 2) void lora_shrink_kernel(ShrinkArgs a)
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
             const int q = (nt0 + n) * 16 + (lane & 15);
-            const u32x4 v = load16(abase + (size_t)min(q, a.r - 1) * a.K + kc * 32);
+            const u32x4 v = load16_stream(abase + (size_t)min(q, a.r - 1) * a.K + kc * 32);
             b[n] = q < a.r ? v : zero16();
         }
     };
@@ -360,9 +364,11 @@ __global__ __launch_bounds__(256, 2) void lora_shrink_kernel(ShrinkArgs a)
         const int r = pass + (lane & 15);
         const bool ok = r < n_rows;
         const int x = a.seg_slots[beg + min(r, n_rows - 1)];
-        const int p = a.exp2perm[x];
-        const uint16_t *aptr =
-            a.X + (size_t)(a.gather_by_token ? x / a.k : p) * a.K + (lane >> 4) * 8;
+        const int xrow = a.gather_by_token ? x / a.k : a.exp2perm[x];
+        const uint16_t *aptr = a.X + (size_t)xrow * a.K + (lane >> 4) * 8;
+        __syncthreads();  // the previous pass's epilogue is done with row_slot
+        if (tid < 16)
+            row_slot[tid] = x;  // for the epilogue (visible after the barriers below)
         auto load_a = [&](int vc, u32x4 (&av)[MT]) {
             const u32x4 v = load16(aptr + (kbeg + vc) * 32);
             av[0] = ok ? v : zero16();
@@ -393,9 +399,8 @@ __global__ __launch_bounds__(256, 2) void lora_shrink_kernel(ShrinkArgs a)
                         (q0 + i + 1 < a.r) ? sum_partials<MT>(part, row, g * 8 + i + 1) : 0.0f;
                     packed[i >> 1] = float_to_bf16_bits(v0) | (float_to_bf16_bits(v1) << 16);
                 }
-                const int xo = a.seg_slots[beg + pass + row];
-                const int po = a.exp2perm[xo];
-                store16(a.S + (size_t)po * a.rp + q0, u32x4{packed[0], packed[1], packed[2], packed[3]});
+                store16(a.S + (size_t)row_slot[row] * a.rp + q0,
+                        u32x4{packed[0], packed[1], packed[2], packed[3]});
             }
         }
     }

@@ -48,7 +48,7 @@ struct ShrinkArgs {
     const uint16_t *A;        // [L, E_l, r, K]
     int r, rp, L, E_l, k;
     const int32_t *seg_offsets, *seg_slots, *exp2perm;
-    uint16_t *S;              // [n, rp], row = permuted index
+    uint16_t *S;              // [n, rp], row = slot x = t * k + j
 };
 
 // Grouped expert GEMM over one packed weight stack, with the LoRA expand
@@ -59,7 +59,7 @@ struct GemmArgs {
     int K;                    // H for gate_up, I for down
     const uint16_t *Wp;       // packed [E_l, NT, K/32, 64, 8]
     int NT;                   // 16-column tiles per expert
-    const uint16_t *S;        // [n, rp] or null
+    const uint16_t *S;        // [n, rp] by slot x, or null
     const uint16_t *LB;       // [L, E_l, n_canon, r] or null
     int r, rp, L, n_canon;
     const int32_t *mapping;   // [T] or null

@@ -3,8 +3,13 @@
 // A [K, N] weight (N contiguous) is rewritten so that the B operand of one
 // 16x16x32 bf16 MFMA -- 32 K rows by 16 columns, lane l holding the 8
 // consecutive K values of column l % 16 starting at row 8 (l / 16) -- is
-// one contiguous 1 KiB block.  The grouped GEMMs then stream each expert's
-// weights with fully coalesced 16-byte loads straight into registers.
+// one contiguous 1 KiB block, and so that everything one GEMM block streams
+// (one 64-column slab of one expert: 4 column tiles over all of K) is one
+// contiguous region, chunk after chunk:
+//   packed[(((e * n_slabs + slab) * KC + kc) * 4 + t) * 512 + 8 l + i]
+//     = W[e][32 kc + 8 (l / 16) + i][col(4 slab + t) + l % 16]
+// The grouped GEMMs then stream each slab with fully coalesced 16-byte loads
+// straight into registers, as one sequential read.
 //
 // For w13 the 16-column tiles alternate gate and up tiles of the same
 // columns (tile 2j = gate columns [16j, 16j+16), tile 2j+1 = the matching up
@@ -26,10 +31,14 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a)
         return;
     const int lane = (int)(f & (kWave - 1));
     size_t rest = f >> 6;
+    const int t = (int)(rest & 3);  // tile inside the 4-tile slab
+    rest >>= 2;
     const int kc = (int)(rest % KC);
     rest /= KC;
-    const int nt = (int)(rest % NT);
-    const int e = (int)(rest / NT);
+    const int n_slabs = NT >> 2;
+    const int slab = (int)(rest % n_slabs);
+    const int e = (int)(rest / n_slabs);
+    const int nt = slab * 4 + t;
     const int col = a.I > 0 ? (nt & 1) * a.I + (nt >> 1) * 16 + (lane & 15)
                             : nt * 16 + (lane & 15);
     const int k0 = kc * 32 + (lane >> 4) * 8;

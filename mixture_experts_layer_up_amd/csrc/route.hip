@@ -7,60 +7,102 @@
 // descending, expert id ascending); weights are the softmax over the k
 // selected logits (renormalised top-k softmax).
 //
-// Selection by counting: the rank of expert e is the number of experts that
-// come before it in that order, {e' : l[e'] > l[e] or (l[e'] == l[e] and
-// e' < e)}.  Ranks are distinct, and rank < k means "selected, at slot rank".
-// Every lane counts independently against the token's logits broadcast from
-// LDS, so there is no chain of dependent cross-lane reductions.
+// Selection as a wave-level radix select.  Each (logit, id) becomes one
+// 42-bit key that orders exactly like (logit descending, id ascending): the
+// order-preserving integer image of the float in the high 32 bits, and
+// 1023 - id in the low 10 bits.  All keys are distinct, so the k-th largest
+// key is found bit by bit from the top, counting keys >= candidate with
+// ballots; the k keys >= it are the selection.  A selected key's slot is the
+// number of selected keys above it.  Every step is a short chain of
+// wave-uniform operations (finite logits assumed).
 #include "device_common.h"
 #include "kernels.h"
 
 namespace moe_lora {
 namespace {
 
-constexpr int kMaxExperts = 1024;
+constexpr int kMaxPerLane = 16;  // up to 1024 experts
 constexpr int kTokensPerBlock = 4;
 
+__device__ __forceinline__ unsigned long long route_key(float v, int e)
+{
+    const uint32_t u = v == 0.0f ? 0u : __float_as_uint(v);  // -0 and +0 compare equal
+    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)ord << 10) | (unsigned long long)(1023 - e);
+}
+
+template <int NV>  // logits per lane: E <= 64 * NV
 __global__ __launch_bounds__(256) void route_topk_kernel(RouteArgs a)
 {
-    __shared__ float logit[kTokensPerBlock][kMaxExperts];
-    __shared__ float sel[kTokensPerBlock][64];
+    __shared__ unsigned long long sel_key[kTokensPerBlock][64];
+    __shared__ float sel_val[kTokensPerBlock][64];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     const int t = blockIdx.x * kTokensPerBlock + wave;
-    const bool active = t < a.T;
-    const int E = a.E;
-    const float *row = a.logits + (size_t)t * E;
-    if (active)
-        for (int e = lane; e < E; e += kWave)
-            logit[wave][e] = row[e];
+    const bool active = t < a.T;  // uniform per wave
+    const int k = a.k;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+
+    unsigned long long key[NV];
+    float val[NV];
+    unsigned long long thr = 0;
+    if (active) {
+        const float *row = a.logits + (size_t)t * a.E;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {  // all loads first, then the keys
+            const int e = lane + kWave * i;
+            val[i] = e < a.E ? row[e] : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = lane + kWave * i;
+            key[i] = e < a.E ? route_key(val[i], e) : 0ull;  // 0 ranks below every real key
+        }
+        // the k-th largest key: the largest threshold with >= k keys at or above it
+        for (int b = 41; b >= 0; --b) {
+            const unsigned long long cand = thr | (1ull << b);
+            int cnt = 0;
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                cnt += __popcll(__ballot(key[i] >= cand));
+            if (cnt >= k)
+                thr = cand;
+        }
+        // compact the k selected keys into LDS (any order)
+        int base = 0;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const bool s = key[i] >= thr;
+            const unsigned long long m = __ballot(s);
+            if (s)
+                sel_key[wave][base + __popcll(m & lt)] = key[i];
+            base += __popcll(m);
+        }
+    }
     __syncthreads();
     if (active) {
-        const float *lw = logit[wave];
-        for (int e = lane; e < E; e += kWave) {
-            const float v = lw[e];
-            int rank = 0;
-            for (int j = 0; j < E; ++j) {
-                const float u = lw[j];
-                rank += (u > v) | ((u == v) & (j < e));
-            }
-            if (rank < a.k) {
-                a.topk_ids[(size_t)t * a.k + rank] = e;
-                sel[wave][rank] = v;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            if (key[i] >= thr) {
+                int slot = 0;
+                for (int q = 0; q < k; ++q)
+                    slot += sel_key[wave][q] > key[i];
+                a.topk_ids[(size_t)t * k + slot] = lane + kWave * i;
+                sel_val[wave][slot] = val[i];
             }
         }
     }
     __syncthreads();
     if (!active)
         return;
-    const float m = sel[wave][0];
-    const float ex = lane < a.k ? expf(sel[wave][lane] - m) : 0.0f;
+    const float m = sel_val[wave][0];
+    const float ex = lane < k ? expf(sel_val[wave][lane] - m) : 0.0f;
     float sum = ex;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1)
         sum += __shfl_xor(sum, off);  // xor butterfly: identical sum on every lane
-    if (lane < a.k)
-        a.topk_weights[(size_t)t * a.k + lane] = ex / sum;
+    if (lane < k)
+        a.topk_weights[(size_t)t * k + lane] = ex / sum;
 }
 
 } // namespace
@@ -70,7 +112,14 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t s)
     if (a.T <= 0)
         return hipSuccess;
     const int blocks = (a.T + kTokensPerBlock - 1) / kTokensPerBlock;
-    hipLaunchKernelGGL(route_topk_kernel, dim3(blocks), dim3(256), 0, s, a);
+    if (a.E <= 64)
+        hipLaunchKernelGGL((route_topk_kernel<1>), dim3(blocks), dim3(256), 0, s, a);
+    else if (a.E <= 128)
+        hipLaunchKernelGGL((route_topk_kernel<2>), dim3(blocks), dim3(256), 0, s, a);
+    else if (a.E <= 256)
+        hipLaunchKernelGGL((route_topk_kernel<4>), dim3(blocks), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((route_topk_kernel<kMaxPerLane>), dim3(blocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

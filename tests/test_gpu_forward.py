@@ -187,3 +187,42 @@ def test_scaling_factor_and_tiny_batches():
         assert got.shape == (T, cfg.hidden)
         if T:
             _compare(cfg, inp, got)
+
+
+def test_hip_graph_replay_matches_eager():
+    """A captured forward replays bitwise equal to eager runs, replay after replay,
+    with eager work and synchronisation between the replays."""
+    announce("forward: HIP graph replay")
+    cfg = CONFIGS["decode64"]
+    inp = cached_inputs("decode64")
+    shape, lay = binding.layer_from_host(cfg, inp)
+    ws = torch.empty(binding.workspace_size(shape), dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    kw = {k: v for k, v in lay.items() if k not in ("hidden", "w13_packed", "w2_packed")}
+
+    def step():
+        binding.forward(shape, lay["hidden"], lay["w13_packed"], lay["w2_packed"], out=out,
+                        workspace=ws, **kw)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        out.fill_(float("nan"))
+        ws.fill_(0x33)              # the forward must not depend on workspace contents
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from eager"
+        step()                      # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)

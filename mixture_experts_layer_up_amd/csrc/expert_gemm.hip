@@ -43,6 +43,15 @@ namespace {
 
 constexpr int kNS = 4;  // 16-column N tiles per block (64 columns)
 
+// Tuning knobs of the decode-shaped (16-row tile) GEMM: K chunks per
+// pipeline stage, and the minimum waves per SIMD the register budget targets.
+#ifndef MOE_LORA_DECODE_CH
+#define MOE_LORA_DECODE_CH 1
+#endif
+#ifndef MOE_LORA_DECODE_WAVES
+#define MOE_LORA_DECODE_WAVES 5
+#endif
+
 template <int MT>
 struct Part {
     static constexpr int kRows = MT * 16;
@@ -149,7 +158,7 @@ __device__ __forceinline__ void run_pipeline(f32x4 (&acc)[MT][NS], int nv, int n
 }
 
 template <int MT, int CH, bool kGated>
-__global__ __launch_bounds__(256, MT == 1 ? 2 : 1) void expert_gemm_kernel(GemmArgs a)
+__global__ __launch_bounds__(256, MT == 1 ? MOE_LORA_DECODE_WAVES : 1) void expert_gemm_kernel(GemmArgs a)
 {
     constexpr int NS = kNS;
     __shared__ float part[Part<MT>::kFloats];
@@ -157,15 +166,21 @@ __global__ __launch_bounds__(256, MT == 1 ? 2 : 1) void expert_gemm_kernel(GemmA
     const int lane = tid & (kWave - 1);
     const int wave = wave_id();
 
+    // Work item -> (expert, slab, row tile).  The items of one expert occupy
+    // logical ids [tb * n_slabs, (tb + nt) * n_slabs); inside that range the
+    // nt row tiles of one slab are adjacent, so blocks that read the same
+    // weight slab are dispatched together on one XCD and share its L2.
     const int logical = xcd_contiguous_index(blockIdx.x, gridDim.x);
-    const int tile = logical / a.n_slabs;
-    const int slab = logical - tile * a.n_slabs;
-    const int4 te = a.tiles[tile];
+    const int4 te = a.tiles[logical / a.n_slabs];
     const int le = te.x;
     if (le < 0)
         return;
-    const int row0 = te.y;
-    const int n_rows = te.z;  // 1 .. 16 * MT
+    const int nt = (te.z + a.tile_rows - 1) / a.tile_rows;
+    const int in_expert = logical - te.w * a.n_slabs;
+    const int slab = in_expert / nt;
+    const int sub = in_expert - slab * nt;
+    const int row0 = te.y + sub * a.tile_rows;
+    const int n_rows = min(a.tile_rows, te.z - sub * a.tile_rows);  // 1 .. 16 * MT
     const int n_mt = (n_rows + 15) >> 4;
 
     // waves take K chunks round-robin (wave w: chunks w, w + 4, ...), so the
@@ -427,13 +442,13 @@ int gemm_tile_rows(int n_slots, int E_l)
 
 hipError_t launch_gemm_gate_up(const GemmArgs &a, hipStream_t s)
 {
-    return a.tile_rows == 16 ? launch_gemm_variant<1, 2, true>(a, s)
+    return a.tile_rows == 16 ? launch_gemm_variant<1, MOE_LORA_DECODE_CH, true>(a, s)
                              : launch_gemm_variant<4, 2, true>(a, s);
 }
 
 hipError_t launch_gemm_down(const GemmArgs &a, hipStream_t s)
 {
-    return a.tile_rows == 16 ? launch_gemm_variant<1, 2, false>(a, s)
+    return a.tile_rows == 16 ? launch_gemm_variant<1, MOE_LORA_DECODE_CH, false>(a, s)
                              : launch_gemm_variant<4, 2, false>(a, s);
 }
 

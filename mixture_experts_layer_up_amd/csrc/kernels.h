@@ -21,9 +21,9 @@ struct PermuteArgs {
     int32_t *expert_counts, *expert_offsets;
     int32_t *exp2perm, *perm2exp;
     int32_t *seg_offsets, *seg_slots;
-    // GEMM work list (optional): one int4 {local expert, first permuted row,
-    // rows, 0} per chunk of at most tile_rows rows of one expert; unused
-    // entries up to max_tiles have expert -1.
+    // GEMM work list (optional): ceil(rows / tile_rows) entries per expert
+    // with rows, each {local expert, its first permuted row, its rows, index
+    // of its first entry}; unused entries up to max_tiles have expert -1.
     int4 *tiles;
     int tile_rows, max_tiles;
 };

@@ -161,8 +161,9 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a)
         for (int i = beg; i < end; ++i) {
             const int first = hist[i];
             const int c = (i + 1 < NK ? hist[i + 1] : total) - first;
+            const int tb = t0;  // every tile of expert i carries the expert's whole range
             for (int r = 0; r < c; r += a.tile_rows)
-                a.tiles[t0++] = make_int4(i, first + r, min(a.tile_rows, c - r), 0);
+                a.tiles[t0++] = make_int4(i, first, c, tb);
         }
         if (tid == kThreads - 1)  // t0 is now the number of tiles
             tile_total = t0;

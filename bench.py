@@ -128,6 +128,99 @@ def algorithmic_cost(cfg, ids, mapping):
     }
 
 
+# --------------------------------------------------------------------------
+# rocprofv3 summaries (written under profiles/, read back for `traffic`)
+# --------------------------------------------------------------------------
+
+PROFILES = os.path.join(ROOT, "profiles")
+GEMM_SOURCES = ["mixture_experts_layer_up_amd/csrc/expert_gemm.hip",
+                "mixture_experts_layer_up_amd/csrc/device_common.h",
+                "mixture_experts_layer_up_amd/csrc/kernels.h"]
+DOMINANT = {"decode": "expert_gemm_kernel<1, 1, true>", "prefill": "expert_gemm_kernel<4, 2, true>"}
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _kernel_short(name: str) -> str:
+    name = name.replace("moe_lora::(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0]
+
+
+def summarize_trace(stats_csv: str, out_md: str, command: str):
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# rocprofv3 kernel trace: {os.path.basename(out_md)[:-3]}", "",
+             f"command: `{command}`", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{_kernel_short(r['Name'])}` | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, out_md: str, command: str,
+                       copy_mib: int, dominant: str):
+    """FETCH_SIZE / WRITE_SIZE per dispatch (median), scaled by what the same
+    counters read for a plain copy kernel (torch.neg) of known size."""
+    import csv
+    import statistics
+
+    def per_kernel(path):
+        agg = {}
+        for r in csv.DictReader(open(path)):
+            agg.setdefault(_kernel_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return agg
+
+    fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
+    copy = [k for k in fetch if "neg_kernel" in k]
+    kib = copy_mib * 1024.0
+    f_scale = kib / max(fetch[copy[0]]) if copy else None
+    w_scale = kib / max(write[copy[0]]) if copy else None
+    lines = [f"# HBM traffic counters: {os.path.basename(out_md)[:-3]}", "",
+             f"command: `{command}` (one rocprofv3 run per counter)", "",
+             f"kernel_source_sha256: {gemm_source_hash()}", "",
+             f"copy calibration (torch.neg over {copy_mib} MiB, reads and writes {kib:.0f} KiB): "
+             f"FETCH_SIZE factor {f_scale:.4f}, WRITE_SIZE factor {w_scale:.4f}", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB |",
+             "|---|---|---|---|---|"]
+    dom_bytes = None
+    for k in fetch:
+        fk = statistics.median(fetch[k])
+        wk = statistics.median(write.get(k, [0.0]))
+        rb, wb = fk * f_scale * 1024, wk * w_scale * 1024
+        lines.append(f"| `{k}` | {fk:.1f} | {wk:.1f} | {rb / 1e6:.2f} | {wb / 1e6:.2f} |")
+        if dominant in k:
+            dom_bytes = rb + wb
+    lines += ["", f"dominant_kernel: `{dominant}`",
+              f"traffic_bytes_per_launch: {dom_bytes:.0f}" if dom_bytes else "traffic_bytes_per_launch: none"]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def traffic_from_profile(workload: str):
+    """Counter-measured HBM bytes per launch of the dominant kernel, if the
+    committed profile was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"gemm_gate_up_swiglu_{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    import re
+    h = re.search(r"kernel_source_sha256: (\w+)", text)
+    b = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    if not h or not b or h.group(1) != gemm_source_hash():
+        return None
+    return int(b.group(1))
+
+
 def cpu_baseline(cfg, inp, min_seconds: float):
     """Time the CPU oracle (as is) on a bounded sample of the same workload."""
     import numpy as np
@@ -158,12 +251,26 @@ def main():
     ap.add_argument("--workload", default="decode64", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle baseline time budget (0 = skip)")
-    ap.add_argument("--graph-steps", type=int, default=200,
-                    help="also time this many steps replayed from a captured HIP graph (0 = skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain copy kernel (torch.neg) over this many MiB, "
                          "to calibrate HBM byte counters against a known size")
+    ap.add_argument("--graph", type=int, default=1,
+                    help="also time the K steps as one HIP-graph replay (1 = yes)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "OUT_MD"),
+                    help="write a kernel-trace summary from rocprofv3 --stats output and exit")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
+                    help="write an HBM counter summary from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--command", default="", help="the profiling command, recorded in summaries")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, command=args.command)
+        return
+    if args.summarize_counters:
+        kind = "prefill" if args.workload == "prefill" else "decode"
+        summarize_counters(*args.summarize_counters, command=args.command,
+                           copy_mib=args.copy_probe_mib or 256, dominant=DOMINANT[kind])
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this layer runs on one GPU; --gpus {args.gpus} is not supported "
@@ -204,55 +311,56 @@ def main():
     torch.cuda.synchronize()
 
     hip = HipEvents()
-    stream = torch.cuda.current_stream().cuda_stream
     K = args.steps
+    nstage = len(binding.STAGE_NAMES)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    # the timed region: K steps launched from the host, each recording its
+    # stage events on the launch stream (per-kernel durations, live)
     evs = [hip.create(binding.NUM_STAGE_EVENTS) for _ in range(K)]
     start, end = hip.create(2)
     log(f"[bench] timing {K} steps")
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     hip.record(start, stream)
-    for s in range(K):
-        step(evs[s])
+    for s_ in range(K):
+        step(evs[s_])
     hip.record(end, stream)
     hip.sync(end)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
-    total_ms = hip.elapsed_ms(start, end)
-    ms_per_step = total_ms / K
-    stage_ms = np.zeros(len(binding.STAGE_NAMES))
-    for s in range(K):
-        for i in range(len(binding.STAGE_NAMES)):
-            stage_ms[i] += hip.elapsed_ms(evs[s][i], evs[s][i + 1])
+    ms_per_step = hip.elapsed_ms(start, end) / K
+    stage_ms = np.zeros(nstage)
+    for s_ in range(K):
+        for i in range(nstage):
+            stage_ms[i] += hip.elapsed_ms(evs[s_][i], evs[s_][i + 1])
     stage_ms /= K
     for e in evs:
         hip.destroy(e)
     hip.destroy([start, end])
 
-    # the same step replayed from a HIP graph (the forward allocates nothing and
-    # never waits on the host, so it captures as-is); reported next to `value`
+    # the same K steps captured into one HIP graph and replayed (the forward
+    # allocates nothing and never waits on the host); reported beside `value`
     graph_ms = None
-    if args.graph_steps > 0:
-        g = torch.cuda.CUDAGraph()
+    if args.graph:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             step()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step()
-        for _ in range(5):
-            g.replay()
+            for _ in range(K):
+                step()
+        g.replay()
         torch.cuda.synchronize()
         gs, ge = hip.create(2)
-        stream = torch.cuda.current_stream().cuda_stream
         hip.record(gs, stream)
-        for _ in range(args.graph_steps):
-            g.replay()
+        g.replay()
         hip.record(ge, stream)
         hip.sync(ge)
-        graph_ms = hip.elapsed_ms(gs, ge) / args.graph_steps
+        graph_ms = hip.elapsed_ms(gs, ge) / K
         hip.destroy([gs, ge])
         del g
         log(f"[bench] graph replay: {graph_ms * 1e3:.1f} us/step")
@@ -295,7 +403,10 @@ def main():
                    "rank": cfg.rank_gate_up, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "gemm_gate_up_swiglu",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic_from_profile(args.workload),
+                     "algorithmic_bytes_per_launch": cost["gate_up_bytes"],
+                     "kernel_us": gate_up_ms * 1e3},
         "layer": {"algorithmic_bytes": cost["bytes"], "flops": cost["flops"],
                   "hbm_gbps": layer_gbps, "hbm_frac": layer_gbps / HBM_PEAK_GBPS,
                   "mfma_tflops": layer_tflops, "mfma_frac": layer_tflops / MFMA_BF16_PEAK_TFLOPS,
@@ -303,6 +414,7 @@ def main():
                   "touched_lora_pairs": cost["touched_lora_pairs"],
                   "local_slots": cost["local_slots"]},
         "stages_us": {n: float(v * 1e3) for n, v in zip(binding.STAGE_NAMES, stage_ms)},
+        "timing": "K host-launched steps between two HIP events on the launch stream",
         "wall_ms_per_step": wall_s * 1e3 / K,
         "graph_replay": None if graph_ms is None else {
             "ms_per_step": graph_ms, "tokens_per_s": cfg.num_tokens / (graph_ms / 1e3),

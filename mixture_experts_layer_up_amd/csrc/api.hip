@@ -88,7 +88,7 @@ Layout make_layout(const moe_lora_shape *s)
     L.perm2exp = take(n * 4);
     L.seg_offsets = take((segs + 1) * 4);
     L.seg_slots = take(n * 4);
-    L.tile_rows = gemm_tile_rows((int)n, (int)el);
+    L.tile_rows = gemm_tile_rows((int)n, (int)el, s->hidden, s->inter);
     L.max_tiles = max_gemm_tiles((int)n, (int)el, L.tile_rows);
     L.tiles = take((size_t)L.max_tiles * sizeof(int4));
     L.s_gu = take(lora_gate_up_active(s) ? n * round8(s->rank_gate_up) * 2 : 0);
@@ -354,7 +354,8 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     g1.k = k;
     g1.I = I;
     g1.Y = act;
-    g1.n_slabs = g1.NT / 4;
+    const int slab_tiles = lay.tile_rows == kDecodeTileRows ? 4 : 8;  // 64 or 128 columns
+    g1.n_slabs = g1.NT / slab_tiles;
     MOE_TRY(check(launch_gemm_gate_up(g1, st)));
     MOE_TRY(record(ev, 3, st));
 
@@ -386,7 +387,7 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     g2.k = k;
     g2.I = I;
     g2.Y = y;
-    g2.n_slabs = g2.NT / 4;
+    g2.n_slabs = g2.NT / slab_tiles;
     MOE_TRY(check(launch_gemm_down(g2, st)));
     MOE_TRY(record(ev, 5, st));
 

@@ -48,6 +48,15 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v)
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// v if cond else 0, without a branch: the load that produced v stays
+// unconditional, so the number of loads in flight is the same on every path
+// and the compiler keeps exact wait counts.
+__device__ __forceinline__ u32x4 keep_if(u32x4 v, bool cond)
+{
+    const unsigned m = cond ? 0xffffffffu : 0u;
+    return u32x4{v.x & m, v.y & m, v.z & m, v.w & m};
+}
+
 __device__ __forceinline__ u32x4 zero16()
 {
     u32x4 z = {0u, 0u, 0u, 0u};
@@ -69,6 +78,26 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c)
 __device__ __forceinline__ int wave_id()
 {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+// Block barrier for LDS traffic only: completes this wave's LDS operations
+// and synchronises the block, but leaves global loads in flight.  A plain
+// __syncthreads() also fences global memory, which waits for every
+// outstanding load and would drain the register prefetch rings.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// A value every lane of the wave holds identically, made scalar so that
+// branches on it are scalar branches.
+__device__ __forceinline__ unsigned long long uniform_u64(unsigned long long v)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((unsigned long long)hi << 32) | lo;
 }
 
 // Blocks are dispatched round-robin over the 8 XCDs (block b runs on XCD

@@ -102,11 +102,13 @@ template <int MT, int NS, int CH>
 struct Stage {
     u32x4 b[CH][NS];
     u32x4 a[CH][MT];
+    bool am[CH][MT];  // applied to a[][] only when the MFMA consumes it
 };
 
 // Two-stage pipeline over virtual chunks [0, nv).  load_b(vc, b[NS]) and
-// load_a(vc, a[MT]) fill one chunk's operands; s0.b may already hold the
-// first stage's B operands (b0_ready).
+// load_a(vc, a[MT], am[MT]) fill one chunk's operands (am: keep-mask of each A
+// fragment, applied at the MFMA so that no load result is consumed early);
+// s0.b may already hold the first stage's B operands (b0_ready).
 template <int MT, int NS, int CH, typename LoadB, typename LoadA>
 __device__ __forceinline__ void run_pipeline(f32x4 (&acc)[MT][NS], int nv, int n_mt,
                                              Stage<MT, NS, CH> &s0, Stage<MT, NS, CH> &s1,
@@ -120,7 +122,7 @@ __device__ __forceinline__ void run_pipeline(f32x4 (&acc)[MT][NS], int nv, int n
             const int vc = min(vc0 + c, nv - 1);
             if (with_b)
                 load_b(vc, st.b[c]);
-            load_a(vc, st.a[c]);
+            load_a(vc, st.a[c], st.am[c]);
         }
     };
     auto compute_stage = [&](const Stage<MT, NS, CH> &st, int vc0) {
@@ -130,9 +132,10 @@ __device__ __forceinline__ void run_pipeline(f32x4 (&acc)[MT][NS], int nv, int n
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     if (m < n_mt) {
+                        const u32x4 av = keep_if(st.a[c][m], st.am[c][m]);
 #pragma unroll
                         for (int n = 0; n < NS; ++n)
-                            acc[m][n] = mfma_16x16x32(st.a[c][m], st.b[c][n], acc[m][n]);
+                            acc[m][n] = mfma_16x16x32(av, st.b[c][n], acc[m][n]);
                     }
                 }
             }
@@ -157,7 +160,7 @@ __device__ __forceinline__ void run_pipeline(f32x4 (&acc)[MT][NS], int nv, int n
     }
 }
 
-template <int MT, int CH, bool kGated>
+template <int MT, int CH, bool kGated, bool kRank8>
 __global__ __launch_bounds__(256, MT == 1 ? MOE_LORA_DECODE_WAVES : 1) void expert_gemm_kernel(GemmArgs a)
 {
     constexpr int NS = kNS;
@@ -195,38 +198,37 @@ __global__ __launch_bounds__(256, MT == 1 ? MOE_LORA_DECODE_WAVES : 1) void expe
     // this block's slab: KC chunks of NS consecutive 1 KiB fragments
     const uint16_t *wbase =
         a.Wp + ((size_t)le * a.n_slabs + slab) * (size_t)KC * NS * 512 + lane * 8;
+    // Branch-free loaders: the address is selected (always a valid one) and
+    // the value masked, so every chunk issues the same loads.
+    const uint16_t *lb = a.LB ? a.LB : a.Wp;
     auto load_b = [&](int vc, u32x4 (&b)[NS]) {
-        if (vc < nm) {
-            const int kc = wave + 4 * vc;
+        const bool main = vc < nm;  // uniform
+        const int kc = wave + 4 * min(vc, nm - 1);
+        const int g = ((vc - nm) * 4 + wave) * 32 + (lane >> 4) * 8;
+        const int aid = main ? 0 : g / a.rp;
+        const int q0 = main ? 0 : g - aid * a.rp;
+        const int aid_c = max(min(aid, a.L - 1), 0);
 #pragma unroll
-            for (int n = 0; n < NS; ++n)
-                b[n] = load16_stream(wbase + ((size_t)kc * NS + n) * 512);
-        } else {
-            const int c = (vc - nm) * 4 + wave;
-            const int g = c * 32 + (lane >> 4) * 8;
-            const int aid = g / a.rp;
-            const int q0 = g - aid * a.rp;
-            const int aid_c = min(aid, a.L - 1);
+        for (int n = 0; n < NS; ++n) {
+            const uint16_t *pm = wbase + ((size_t)kc * NS + n) * 512;
+            const int col = kGated ? (n & 1) * a.I + (slab * 2 + (n >> 1)) * 16 + (lane & 15)
+                                   : (slab * NS + n) * 16 + (lane & 15);
+            const uint16_t *pe = lb + (((size_t)aid_c * a.E_l + le) * a.n_canon + col) * a.r;
+            if (kRank8) {
+                // past the last adapter (aid >= L) the clamped stack is read; its
+                // K positions meet zero activations, so it adds nothing
+                b[n] = load16_stream(main ? pm : pe + q0);
+            } else {  // rank not a multiple of 8: the expand rows need 2-byte loads
+                const u32x4 vm = load16_stream(pm);
+                uint32_t w[4];
 #pragma unroll
-            for (int n = 0; n < NS; ++n) {
-                const int col = kGated ? (n & 1) * a.I + (slab * 2 + (n >> 1)) * 16 + (lane & 15)
-                                       : (slab * NS + n) * 16 + (lane & 15);
-                const uint16_t *src =
-                    a.LB + (((size_t)aid_c * a.E_l + le) * a.n_canon + col) * a.r;
-                u32x4 v;
-                if ((a.r & 7) == 0) {
-                    v = load16_stream(src + q0);
-                } else {
-                    uint32_t w[4];
-#pragma unroll
-                    for (int i = 0; i < 8; i += 2) {
-                        const uint32_t lo = src[min(q0 + i, a.r - 1)];
-                        const uint32_t hi = src[min(q0 + i + 1, a.r - 1)];
-                        w[i >> 1] = (q0 + i < a.r ? lo : 0u) | ((q0 + i + 1 < a.r ? hi : 0u) << 16);
-                    }
-                    v = u32x4{w[0], w[1], w[2], w[3]};
+                for (int i = 0; i < 8; i += 2) {
+                    const uint32_t lo = pe[min(q0 + i, a.r - 1)];
+                    const uint32_t hi = pe[min(q0 + i + 1, a.r - 1)];
+                    w[i >> 1] = (q0 + i < a.r ? lo : 0u) | ((q0 + i + 1 < a.r ? hi : 0u) << 16);
                 }
-                b[n] = aid < a.L ? v : zero16();
+                const u32x4 ve = keep_if(u32x4{w[0], w[1], w[2], w[3]}, aid < a.L);
+                b[n] = main ? vm : ve;
             }
         }
     };
@@ -241,13 +243,11 @@ __global__ __launch_bounds__(256, MT == 1 ? MOE_LORA_DECODE_WAVES : 1) void expe
 
     // rows of this tile; lanes past the tile's rows read a clamped valid row
     const uint16_t *aptr[MT];
-    bool ok[MT];
     int xslot[MT];
     int adapter[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
         const int r = m * 16 + (lane & 15);
-        ok[m] = r < n_rows;
         const int p = row0 + min(r, n_rows - 1);
         const int x = a.perm2exp[p];
         xslot[m] = x;
@@ -256,27 +256,21 @@ __global__ __launch_bounds__(256, MT == 1 ? MOE_LORA_DECODE_WAVES : 1) void expe
         const int l = (lora && a.mapping) ? a.mapping[tok] : -1;
         adapter[m] = (l >= 0 && l < a.L) ? l : -1;
     }
-    auto load_a = [&](int vc, u32x4 (&av)[MT]) {
-        if (vc < nm) {
-            const int kc = wave + 4 * vc;
+    // rows past the tile read a clamped valid row and are never stored: main
+    // chunks need no mask; expand chunks keep only the row's own adapter block
+    const uint16_t *sbase = a.S ? a.S : a.X;
+    auto load_a = [&](int vc, u32x4 (&av)[MT], bool (&am)[MT]) {
+        const bool main = vc < nm;  // uniform
+        const int kc = wave + 4 * min(vc, nm - 1);
+        const int g = ((vc - nm) * 4 + wave) * 32 + (lane >> 4) * 8;
+        const int aid = main ? -1 : g / a.rp;
+        const int q0 = main ? 0 : g - aid * a.rp;
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                if (m < n_mt) {
-                    const u32x4 v = load16(aptr[m] + kc * 32);
-                    av[m] = ok[m] ? v : zero16();
-                }
-            }
-        } else {
-            const int c = (vc - nm) * 4 + wave;
-            const int g = c * 32 + (lane >> 4) * 8;
-            const int aid = g / a.rp;
-            const int q0 = g - aid * a.rp;
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                if (m < n_mt) {
-                    const u32x4 v = load16(a.S + (size_t)xslot[m] * a.rp + q0);
-                    av[m] = (ok[m] && adapter[m] == aid) ? v : zero16();
-                }
+        for (int m = 0; m < MT; ++m) {
+            if (m < n_mt) {
+                const uint16_t *pa = main ? aptr[m] + kc * 32 : sbase + (size_t)xslot[m] * a.rp + q0;
+                av[m] = load16(pa);
+                am[m] = main || adapter[m] == aid;
             }
         }
     };
@@ -356,8 +350,8 @@ __global__ __launch_bounds__(256, 2) void lora_shrink_kernel(ShrinkArgs a)
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
             const int q = (nt0 + n) * 16 + (lane & 15);
-            const u32x4 v = load16_stream(abase + (size_t)min(q, a.r - 1) * a.K + kc * 32);
-            b[n] = q < a.r ? v : zero16();
+            // q >= r reads a clamped valid row; those output columns are not stored
+            b[n] = load16_stream(abase + (size_t)min(q, a.r - 1) * a.K + kc * 32);
         }
     };
     const int beg = a.seg_offsets[seg];
@@ -377,16 +371,15 @@ __global__ __launch_bounds__(256, 2) void lora_shrink_kernel(ShrinkArgs a)
     for (int pass = 0; pass < n_rows; pass += 16) {
         const int rows = min(16, n_rows - pass);
         const int r = pass + (lane & 15);
-        const bool ok = r < n_rows;
         const int x = a.seg_slots[beg + min(r, n_rows - 1)];
         const int xrow = a.gather_by_token ? x / a.k : a.exp2perm[x];
         const uint16_t *aptr = a.X + (size_t)xrow * a.K + (lane >> 4) * 8;
-        __syncthreads();  // the previous pass's epilogue is done with row_slot
+        lds_barrier();  // the previous pass's epilogue is done with row_slot
         if (tid < 16)
             row_slot[tid] = x;  // for the epilogue (visible after the barriers below)
-        auto load_a = [&](int vc, u32x4 (&av)[MT]) {
-            const u32x4 v = load16(aptr + (kbeg + vc) * 32);
-            av[0] = ok ? v : zero16();
+        auto load_a = [&](int vc, u32x4 (&av)[MT], bool (&am)[MT]) {
+            av[0] = load16(aptr + (kbeg + vc) * 32);  // rows past the segment: not stored
+            am[0] = true;
         };
         for (int nt0 = 0; nt0 < n_nt; nt0 += NS) {
             auto load_b = [&](int vc, u32x4 (&b)[NS]) { load_b_nt(nt0, vc, b); };
@@ -395,9 +388,9 @@ __global__ __launch_bounds__(256, 2) void lora_shrink_kernel(ShrinkArgs a)
             run_pipeline<MT, NS, CH>(acc, nm, 1, s0, s1, first && early, load_b, load_a);
             first = false;
 
-            __syncthreads();  // the previous epilogue is done with `part`
+            lds_barrier();  // the previous epilogue is done with `part`
             store_partials<MT, NS>(part, acc, 1, wave, lane);
-            __syncthreads();
+            lds_barrier();
 
             const int groups = min(NS, n_nt - nt0) * 2;  // 8-wide q groups
             for (int item = tid; item < rows * groups; item += 256) {
@@ -427,29 +420,31 @@ hipError_t launch_gemm_variant(const GemmArgs &a, hipStream_t s)
     const int blocks = a.n_tiles * a.n_slabs;
     if (blocks <= 0)
         return hipSuccess;
-    hipLaunchKernelGGL((expert_gemm_kernel<MT, CH, kGated>), dim3(blocks), dim3(256), 0, s, a);
+    if ((a.r & 7) == 0)
+        hipLaunchKernelGGL((expert_gemm_kernel<MT, CH, kGated, true>), dim3(blocks), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((expert_gemm_kernel<MT, CH, kGated, false>), dim3(blocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 } // namespace
 
-int gemm_tile_rows(int n_slots, int E_l)
+int gemm_tile_rows(int n_slots, int E_l, int H, int I)
 {
-    // rows per tile: 16 for decode-like batches (few rows per expert), 64
-    // when experts carry many rows (fewer re-reads of each weight slab)
-    return n_slots >= 32 * E_l ? 64 : 16;
+    // the wide kernel once experts average 32 or more rows
+    return (n_slots >= 32 * E_l && gemm_wide_supported(H, I)) ? kWideTileRows : kDecodeTileRows;
 }
 
 hipError_t launch_gemm_gate_up(const GemmArgs &a, hipStream_t s)
 {
-    return a.tile_rows == 16 ? launch_gemm_variant<1, MOE_LORA_DECODE_CH, true>(a, s)
-                             : launch_gemm_variant<4, 2, true>(a, s);
+    return a.tile_rows == kDecodeTileRows ? launch_gemm_variant<1, MOE_LORA_DECODE_CH, true>(a, s)
+                                          : launch_gemm_wide(a, true, s);
 }
 
 hipError_t launch_gemm_down(const GemmArgs &a, hipStream_t s)
 {
-    return a.tile_rows == 16 ? launch_gemm_variant<1, MOE_LORA_DECODE_CH, false>(a, s)
-                             : launch_gemm_variant<4, 2, false>(a, s);
+    return a.tile_rows == kDecodeTileRows ? launch_gemm_variant<1, MOE_LORA_DECODE_CH, false>(a, s)
+                                          : launch_gemm_wide(a, false, s);
 }
 
 hipError_t launch_shrink(const ShrinkArgs &a, hipStream_t s)

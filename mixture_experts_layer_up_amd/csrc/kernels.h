@@ -71,8 +71,14 @@ struct GemmArgs {
     int n_slabs;
 };
 
-// Rows per GEMM work-list tile for n local slots over E_l experts (16 or 64).
-int gemm_tile_rows(int n_slots, int E_l);
+// Rows per GEMM work-list tile: 16 for the decode-shaped kernel (few rows
+// per expert), 160 for the wide kernel (many rows per expert, when the
+// shape allows it).
+constexpr int kDecodeTileRows = 16;
+constexpr int kWideTileRows = 160;
+bool gemm_wide_supported(int H, int I);
+int gemm_tile_rows(int n_slots, int E_l, int H, int I);
+hipError_t launch_gemm_wide(const GemmArgs &a, bool gated, hipStream_t s);
 
 struct FinalizeArgs {
     const uint16_t *Y;        // [n, H]

@@ -24,26 +24,101 @@ def _device_asm(src, tmp_path):
     return out.read_text()
 
 
+_LABEL = re.compile(r"^(\.LBB\S+|_Z\S+):")
+_BRANCH = re.compile(r"^s_(cbranch_\w+|branch)\s+(\S+)")
+
+
+def _exec_effect(t):
+    """New 'EXEC narrowed' state after instruction t, or None if unchanged."""
+    if re.match(r"s_(and|andn2|or|xor)_saveexec_b64", t):
+        return True
+    if re.match(r"s_(xor|andn2|and)_b64\s+exec,", t):
+        return True
+    if re.match(r"s_(or|mov)_b64\s+exec,", t):
+        return False
+    return None
+
+
 def _mfma_under_exec_mask(asm):
-    """(kernel, line) of every MFMA issued while EXEC is narrowed."""
+    """(kernel, line) of every MFMA that can be reached while EXEC is narrowed.
+
+    The compiler places masked regions out of line and jumps back, so the
+    check follows the control flow: the kernel is cut into basic blocks, and
+    'EXEC narrowed' is propagated along every edge (a saveexec or an exec
+    and/xor/andn2 narrows it, an exec or/mov restores it; the taken edge of
+    s_cbranch_execz exists only while it is narrowed) until nothing changes.
+    """
     bad, total = [], 0
-    kernel, masked = None, False
+    kernels, cur = [], None
     for ln in asm.splitlines():
+        t = ln.split(";")[0].strip()
         m = re.match(r"^(_Z\S+):", ln)
         if m:
-            kernel, masked = m.group(1), False
+            cur = (m.group(1), [])
+            kernels.append(cur)
             continue
-        t = ln.strip()
-        if t.startswith("s_and_saveexec") or t.startswith("s_andn2_saveexec"):
-            masked = True
-        elif re.match(r"s_(or|mov)_b64\s+exec,", t):
-            masked = False
-        elif t.startswith("v_mfma"):
-            total += 1
-            if masked:
-                bad.append((kernel, t))
-        elif t.startswith("s_endpgm"):
-            kernel, masked = None, False
+        if cur is None:
+            continue
+        if t.startswith("s_endpgm"):
+            cur[1].append(t)
+            cur = None
+            continue
+        if t:
+            cur[1].append(t)
+    for name, lines in kernels:
+        blocks, labels = [[]], {}
+        for t in lines:
+            lab = re.match(r"^(\.LBB\S+):", t)
+            if lab:
+                if blocks[-1]:
+                    blocks.append([])
+                labels[lab.group(1)] = len(blocks) - 1
+                continue
+            blocks[-1].append(t)
+            if _BRANCH.match(t) or t.startswith("s_endpgm"):
+                blocks.append([])
+        entry = [False] * len(blocks)
+        seen = [False] * len(blocks)
+        seen[0] = True
+        work = [0]
+        while work:
+            b = work.pop()
+            state = entry[b]
+            succ = []
+            falls = True
+            for t in blocks[b]:
+                eff = _exec_effect(t)
+                if eff is not None:
+                    state = eff
+                br = _BRANCH.match(t)
+                if br:
+                    kind, target = br.groups()
+                    # s_cbranch_execz is taken only when EXEC is empty, which
+                    # cannot happen while it is whole: that edge exists only
+                    # inside a narrowed region
+                    if target in labels and (kind != "cbranch_execz" or state):
+                        succ.append((labels[target], state))
+                    if kind == "branch":
+                        falls = False
+                if t.startswith("s_endpgm"):
+                    falls = False
+            if falls and b + 1 < len(blocks):
+                succ.append((b + 1, state))
+            for nb, st in succ:
+                if not seen[nb] or (st and not entry[nb]):
+                    seen[nb] = True
+                    entry[nb] = entry[nb] or st
+                    work.append(nb)
+        for b, blk in enumerate(blocks):
+            state = entry[b]
+            for t in blk:
+                eff = _exec_effect(t)
+                if eff is not None:
+                    state = eff
+                if t.startswith("v_mfma"):
+                    total += 1
+                    if state and seen[b]:
+                        bad.append((name, t))
     return bad, total
 
 

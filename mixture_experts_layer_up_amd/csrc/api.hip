@@ -63,7 +63,7 @@ bool lora_down_active(const moe_lora_shape *s) { return s->num_loras > 0 && s->r
 // Workspace regions; every offset is a multiple of 256 bytes.
 struct Layout {
     size_t ids, weights, counts, offsets, exp2perm, perm2exp, seg_offsets, seg_slots;
-    size_t tiles, s_gu, act, s_dn, y;
+    size_t tiles, tile_count, zeros, s_gu, act, s_dn, y;
     int tile_rows, max_tiles;
     size_t total;
 };
@@ -88,9 +88,13 @@ Layout make_layout(const moe_lora_shape *s)
     L.perm2exp = take(n * 4);
     L.seg_offsets = take((segs + 1) * 4);
     L.seg_slots = take(n * 4);
-    L.tile_rows = gemm_tile_rows((int)n, (int)el, s->hidden, s->inter);
+    L.tile_rows = gemm_tile_rows((int)n, (int)el, s->hidden, s->inter,
+                                 lora_gate_up_active(s) ? s->rank_gate_up : 0,
+                                 lora_down_active(s) ? s->rank_down : 0);
     L.max_tiles = max_gemm_tiles((int)n, (int)el, L.tile_rows);
     L.tiles = take((size_t)L.max_tiles * sizeof(int4));
+    L.tile_count = take(sizeof(int32_t));
+    L.zeros = take(kZeroBytes);
     L.s_gu = take(lora_gate_up_active(s) ? n * round8(s->rank_gate_up) * 2 : 0);
     L.act = take(n * (size_t)s->inter * 2);
     L.s_dn = take(lora_down_active(s) ? n * round8(s->rank_down) * 2 : 0);
@@ -116,7 +120,8 @@ struct RoutingPtrs {
 
 int enqueue_routing(const moe_lora_shape *s, const float *logits, const int32_t *topk_ids,
                     const int32_t *mapping, const RoutingPtrs &r, hipStream_t st,
-                    int4 *tiles = nullptr, int tile_rows = 0, int max_tiles = 0)
+                    int4 *tiles = nullptr, int tile_rows = 0, int max_tiles = 0,
+                    int32_t *tile_count = nullptr, void *zeros = nullptr)
 {
     if (logits) {
         RouteArgs ra{logits, r.ids, r.weights, s->num_tokens, s->num_experts, s->top_k};
@@ -139,6 +144,8 @@ int enqueue_routing(const moe_lora_shape *s, const float *logits, const int32_t 
     pa.tiles = tiles;
     pa.tile_rows = tile_rows;
     pa.max_tiles = max_tiles;
+    pa.tile_count = tile_count;
+    pa.zeros = static_cast<u32x4_t *>(zeros);
     return check(launch_permute(pa, st));
 }
 
@@ -322,8 +329,10 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
 
     MOE_TRY(record(ev, 0, st));
     int4 *tiles = reinterpret_cast<int4 *>(ws + lay.tiles);
+    void *zeros = ws + lay.zeros;
+    int32_t *tile_count = reinterpret_cast<int32_t *>(ws + lay.tile_count);
     MOE_TRY(enqueue_routing(shape, in->router_logits, in->topk_ids, in->token_lora_mapping, r, st,
-                            tiles, lay.tile_rows, lay.max_tiles));
+                            tiles, lay.tile_rows, lay.max_tiles, tile_count, zeros));
     MOE_TRY(record(ev, 1, st));
 
     if (gu) {
@@ -347,6 +356,7 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     g1.n_canon = 2 * I;
     g1.mapping = in->token_lora_mapping;
     g1.tiles = tiles;
+    g1.tile_count = tile_count;
     g1.n_tiles = lay.max_tiles;
     g1.tile_rows = lay.tile_rows;
     g1.perm2exp = r.perm2exp;
@@ -356,6 +366,7 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     g1.Y = act;
     const int slab_tiles = lay.tile_rows == kDecodeTileRows ? 4 : 8;  // 64 or 128 columns
     g1.n_slabs = g1.NT / slab_tiles;
+    g1.zeros = static_cast<const uint16_t *>(zeros);
     MOE_TRY(check(launch_gemm_gate_up(g1, st)));
     MOE_TRY(record(ev, 3, st));
 
@@ -380,6 +391,7 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     g2.n_canon = H;
     g2.mapping = in->token_lora_mapping;
     g2.tiles = tiles;
+    g2.tile_count = tile_count;
     g2.n_tiles = lay.max_tiles;
     g2.tile_rows = lay.tile_rows;
     g2.perm2exp = r.perm2exp;
@@ -388,6 +400,7 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     g2.I = I;
     g2.Y = y;
     g2.n_slabs = g2.NT / slab_tiles;
+    g2.zeros = static_cast<const uint16_t *>(zeros);
     MOE_TRY(check(launch_gemm_down(g2, st)));
     MOE_TRY(record(ev, 5, st));
 

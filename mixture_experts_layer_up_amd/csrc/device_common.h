@@ -101,16 +101,20 @@ __device__ __forceinline__ unsigned long long uniform_u64(unsigned long long v)
 }
 
 // Blocks are dispatched round-robin over the 8 XCDs (block b runs on XCD
-// b % 8).  Renumber so that each XCD receives one contiguous range of
-// logical work items: neighbouring items (for example the column slabs of
-// one expert, which share activation rows) then share that XCD's L2.
-__device__ __forceinline__ int xcd_contiguous_index(int bid, int n)
+// b % 8).  The grid is an upper bound of the work; the n_items work items
+// (a count known only on the device) are split into 8 equal contiguous
+// ranges, one per XCD, so that the real work is spread evenly over the XCDs
+// however many blocks are spare, and neighbouring items (for example the
+// column slabs of one expert, which share activation rows) share that XCD's
+// L2.  Returns -1 for a block without work.
+__device__ __forceinline__ int xcd_balanced_item(int bid, int n_items)
 {
-    const int xcd = bid & 7;
+    const int per = (n_items + 7) >> 3;
     const int idx = bid >> 3;
-    const int per = n >> 3;
-    const int rem = n & 7;
-    return xcd * per + (xcd < rem ? xcd : rem) + idx;
+    if (idx >= per)
+        return -1;
+    const int item = (bid & 7) * per + idx;
+    return item < n_items ? item : -1;
 }
 
 __device__ __forceinline__ float silu_f32(float z)

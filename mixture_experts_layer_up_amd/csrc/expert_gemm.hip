@@ -173,7 +173,9 @@ __global__ __launch_bounds__(256, MT == 1 ? MOE_LORA_DECODE_WAVES : 1) void expe
     // logical ids [tb * n_slabs, (tb + nt) * n_slabs); inside that range the
     // nt row tiles of one slab are adjacent, so blocks that read the same
     // weight slab are dispatched together on one XCD and share its L2.
-    const int logical = xcd_contiguous_index(blockIdx.x, gridDim.x);
+    const int logical = xcd_balanced_item(blockIdx.x, *a.tile_count * a.n_slabs);
+    if (logical < 0)
+        return;
     const int4 te = a.tiles[logical / a.n_slabs];
     const int le = te.x;
     if (le < 0)
@@ -429,10 +431,11 @@ hipError_t launch_gemm_variant(const GemmArgs &a, hipStream_t s)
 
 } // namespace
 
-int gemm_tile_rows(int n_slots, int E_l, int H, int I)
+int gemm_tile_rows(int n_slots, int E_l, int H, int I, int r_gu, int r_dn)
 {
     // the wide kernel once experts average 32 or more rows
-    return (n_slots >= 32 * E_l && gemm_wide_supported(H, I)) ? kWideTileRows : kDecodeTileRows;
+    return (n_slots >= 32 * E_l && gemm_wide_supported(H, I, r_gu, r_dn)) ? kWideTileRows
+                                                                          : kDecodeTileRows;
 }
 
 hipError_t launch_gemm_gate_up(const GemmArgs &a, hipStream_t s)

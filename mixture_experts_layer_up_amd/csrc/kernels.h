@@ -14,6 +14,8 @@ struct RouteArgs {
     int T, E, k;
 };
 
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+
 struct PermuteArgs {
     const int32_t *topk_ids;   // [T*k]
     const int32_t *mapping;    // [T] or null
@@ -26,7 +28,13 @@ struct PermuteArgs {
     // of its first entry}; unused entries up to max_tiles have expert -1.
     int4 *tiles;
     int tile_rows, max_tiles;
+    int32_t *tile_count;       // number of used work-list entries
+    u32x4_t *zeros;            // kZeroBytes written as zero (for the GEMMs)
 };
+
+// A small all-zero region of the workspace, rewritten by every permute
+// launch; the wide GEMM's direct loads read it in place of masked values.
+constexpr int kZeroBytes = 1024;
 
 // Upper bound on the GEMM work-list length for n slots and E_l experts.
 inline int max_gemm_tiles(int n, int E_l, int tile_rows)
@@ -64,11 +72,13 @@ struct GemmArgs {
     int r, rp, L, n_canon;
     const int32_t *mapping;   // [T] or null
     const int4 *tiles;        // work list written by the permute kernel
+    const int32_t *tile_count; // its used length, written by the permute kernel
     int n_tiles, tile_rows;   // list length (upper bound), rows per tile
     const int32_t *perm2exp;  // [n]
     int E_l, k, I;
     uint16_t *Y;              // gated: act [n, I]; else y [n, n_canon]
     int n_slabs;
+    const uint16_t *zeros;    // kZeroBytes of zeros
 };
 
 // Rows per GEMM work-list tile: 16 for the decode-shaped kernel (few rows
@@ -76,8 +86,9 @@ struct GemmArgs {
 // shape allows it).
 constexpr int kDecodeTileRows = 16;
 constexpr int kWideTileRows = 160;
-bool gemm_wide_supported(int H, int I);
-int gemm_tile_rows(int n_slots, int E_l, int H, int I);
+// r_gu, r_dn: ranks of the active LoRA projections (0 when inactive)
+bool gemm_wide_supported(int H, int I, int r_gu, int r_dn);
+int gemm_tile_rows(int n_slots, int E_l, int H, int I, int r_gu, int r_dn);
 hipError_t launch_gemm_wide(const GemmArgs &a, bool gated, hipStream_t s);
 
 struct FinalizeArgs {

@@ -56,6 +56,8 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a)
     const int NK = by_segment ? a.L * a.E_l : a.E_l;
     int32_t *out_offsets = by_segment ? a.seg_offsets : a.expert_offsets;
     int32_t *out_list = by_segment ? a.seg_slots : a.perm2exp;
+    if (!by_segment && a.zeros && tid < kZeroBytes / 16)
+        a.zeros[tid] = u32x4_t{0u, 0u, 0u, 0u};
 
     if (NK == 0) {  // no adapters: empty segment list
         if (tid == 0)
@@ -165,8 +167,11 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a)
             for (int r = 0; r < c; r += a.tile_rows)
                 a.tiles[t0++] = make_int4(i, first, c, tb);
         }
-        if (tid == kThreads - 1)  // t0 is now the number of tiles
+        if (tid == kThreads - 1) {  // t0 is now the number of tiles
             tile_total = t0;
+            if (a.tile_count)
+                *a.tile_count = t0;
+        }
         __syncthreads();
         for (int i = tile_total + tid; i < a.max_tiles; i += kThreads)
             a.tiles[i] = make_int4(-1, 0, 0, 0);

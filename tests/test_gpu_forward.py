@@ -29,6 +29,16 @@ MID_EP = MID.replace(name="mid_ep", local_expert_offset=5, local_num_experts=7, 
 BIG_ROWS = LayerConfig("big_rows", 300, 128, 64, 4, 1, 0, 4, 2, 16, 16, seed=34,
                        mapping="uniform", sigma_lora_a=0.2, sigma_lora_b=0.2)
 TINY_AMP = CONFIGS["tiny"].replace(name="tiny_amp", sigma_lora_a=0.2, sigma_lora_b=0.2)
+# Many rows per expert (the 160-row tile kernel): ~350 rows per expert, so
+# three row tiles with a ragged last one; 3 adapters of rank 24, so a K chunk
+# of the LoRA expand spans two adapters and the last chunk is partial; tokens
+# without adapter leave some 16-row tiles out of the expand.
+WIDE = LayerConfig("wide", 700, 256, 192, 4, 2, 0, 4, 3, 24, 24, seed=35, mapping="uniform",
+                   sigma_lora_a=0.1, sigma_lora_b=0.1)
+# one rank-8 adapter (a single, mostly empty expand chunk), adapter in runs
+WIDE_R8 = WIDE.replace(name="wide_r8", num_tokens=520, num_loras=1, rank_gate_up=8,
+                       rank_down=8, mapping="runs", run_length=130, seed=36,
+                       sigma_lora_a=0.2, sigma_lora_b=0.2)
 
 
 def _compare(cfg, inp, got, tokens=None, **kw):
@@ -63,7 +73,7 @@ def test_prefill_sampled_tokens():
     _compare(cfg, inp, got, tokens=toks)
 
 
-@pytest.mark.parametrize("cfg", [MID, MID_R64, MID_EP, BIG_ROWS, TINY_AMP],
+@pytest.mark.parametrize("cfg", [MID, MID_R64, MID_EP, BIG_ROWS, TINY_AMP, WIDE, WIDE_R8],
                          ids=lambda c: c.name)
 def test_small_shapes_and_lora_delta(cfg):
     announce(f"forward {cfg.name}")

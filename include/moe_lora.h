@@ -134,7 +134,9 @@ typedef struct moe_lora_routing {
  *   stage_events       NULL, or MOE_LORA_NUM_STAGE_EVENTS hipEvent_t handles
  *                      recorded on `stream` at the stage boundaries (for
  *                      per-kernel timing); stages that do not run still get
- *                      their event recorded
+ *                      their event recorded; a NULL entry is skipped (each
+ *                      recorded event costs a few microseconds of stream
+ *                      time, so record only the boundaries you need)
  * LoRA pointers may be NULL when the projection is inactive.
  */
 typedef struct moe_lora_inputs {

@@ -171,7 +171,7 @@ int enqueue_empty_batch(const moe_lora_shape *s, const moe_lora_routing *routing
 
 int record(void *const *events, int i, hipStream_t st)
 {
-    if (!events)
+    if (!events || !events[i])
         return MOE_LORA_OK;
     return check(hipEventRecord(static_cast<hipEvent_t>(events[i]), st));
 }
@@ -337,7 +337,8 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
 
     if (gu) {
         ShrinkArgs sa{hidden, 1, H, static_cast<const uint16_t *>(in->lora_a_gate_up),
-                      rg, round8(rg), L, E_l, k, r.seg_offsets, r.seg_slots, r.exp2perm, s_gu};
+                      rg, round8(rg), L, E_l, k, r.seg_offsets, r.seg_slots, r.exp2perm, s_gu,
+                      T * k};
         MOE_TRY(check(launch_shrink(sa, st)));
     }
     MOE_TRY(record(ev, 2, st));
@@ -364,15 +365,17 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     g1.k = k;
     g1.I = I;
     g1.Y = act;
-    const int slab_tiles = lay.tile_rows == kDecodeTileRows ? 4 : 8;  // 64 or 128 columns
-    g1.n_slabs = g1.NT / slab_tiles;
+    // column slabs per expert: 64 columns (decode kernel) or 128 (wide kernel)
+    auto slabs = [&](int NT) { return lay.tile_rows == kDecodeTileRows ? NT / 4 : NT / 8; };
+    g1.n_slabs = slabs(g1.NT);
     g1.zeros = static_cast<const uint16_t *>(zeros);
     MOE_TRY(check(launch_gemm_gate_up(g1, st)));
     MOE_TRY(record(ev, 3, st));
 
     if (dn) {
         ShrinkArgs sa{act, 0, I, static_cast<const uint16_t *>(in->lora_a_down),
-                      rd, round8(rd), L, E_l, k, r.seg_offsets, r.seg_slots, r.exp2perm, s_dn};
+                      rd, round8(rd), L, E_l, k, r.seg_offsets, r.seg_slots, r.exp2perm, s_dn,
+                      T * k};
         MOE_TRY(check(launch_shrink(sa, st)));
     }
     MOE_TRY(record(ev, 4, st));
@@ -399,7 +402,7 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     g2.k = k;
     g2.I = I;
     g2.Y = y;
-    g2.n_slabs = g2.NT / slab_tiles;
+    g2.n_slabs = slabs(g2.NT);
     g2.zeros = static_cast<const uint16_t *>(zeros);
     MOE_TRY(check(launch_gemm_down(g2, st)));
     MOE_TRY(record(ev, 5, st));

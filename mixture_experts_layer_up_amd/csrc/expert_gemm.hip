@@ -161,7 +161,7 @@ __device__ __forceinline__ void run_pipeline(f32x4 (&acc)[MT][NS], int nv, int n
 }
 
 template <int MT, int CH, bool kGated, bool kRank8>
-__global__ __launch_bounds__(256, MT == 1 ? MOE_LORA_DECODE_WAVES : 1) void expert_gemm_kernel(GemmArgs a)
+__global__ __launch_bounds__(256, MT == 1 ? (kRank8 ? MOE_LORA_DECODE_WAVES : 3) : 1) void expert_gemm_kernel(GemmArgs a)
 {
     constexpr int NS = kNS;
     __shared__ float part[Part<MT>::kFloats];
@@ -324,17 +324,18 @@ __global__ __launch_bounds__(256, MT == 1 ? MOE_LORA_DECODE_WAVES : 1) void expe
 }
 
 // LoRA shrink: S[x, 0:rp] = A[l, e] x_row for the slots x of one virtual
-// expert (adapter l, local expert e) per block, 16 rows per pass; q >= r is
-// written as 0.  S is indexed by slot, so the gate_up shrink (rows = the
-// slots' tokens) needs no permutation lookup at all.  The stack A[l, e] (r x K) is K-contiguous per rank row, which is
-// exactly the per-lane B operand layout of the MFMA (8 consecutive K values of
-// one column q).  NS 16-column tiles of q per pass over N.
-template <int NS, int CH>
+// expert (adapter l, local expert e) per block, 16 * MT rows per pass; q >= r
+// is written as 0.  S is indexed by slot, so the gate_up shrink (rows = the
+// slots' tokens) needs no permutation lookup at all.  The stack A[l, e]
+// (r x K) is K-contiguous per rank row, which is exactly the per-lane B
+// operand layout of the MFMA (8 consecutive K values of one column q).  NS
+// 16-column tiles of q per pass over N; the 4 waves split K.
+template <int NS, int CH, int MT>
 __global__ __launch_bounds__(256, 2) void lora_shrink_kernel(ShrinkArgs a)
 {
-    constexpr int MT = 1;
+    constexpr int kRows = 16 * MT;
     __shared__ float part[Part<MT>::kFloats];
-    __shared__ int row_slot[16];
+    __shared__ int row_slot[kRows];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = wave_id();
@@ -370,28 +371,39 @@ __global__ __launch_bounds__(256, 2) void lora_shrink_kernel(ShrinkArgs a)
     }
 
     bool first = true;
-    for (int pass = 0; pass < n_rows; pass += 16) {
-        const int rows = min(16, n_rows - pass);
-        const int r = pass + (lane & 15);
-        const int x = a.seg_slots[beg + min(r, n_rows - 1)];
-        const int xrow = a.gather_by_token ? x / a.k : a.exp2perm[x];
-        const uint16_t *aptr = a.X + (size_t)xrow * a.K + (lane >> 4) * 8;
+    for (int pass = 0; pass < n_rows; pass += kRows) {
+        const int rows = min(kRows, n_rows - pass);
+        const int n_mt = (rows + 15) >> 4;
+        // this lane's row in each M tile (past the segment: its last row,
+        // computed but never stored)
+        const uint16_t *aptr[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int x = a.seg_slots[beg + min(pass + m * 16 + (lane & 15), n_rows - 1)];
+            const int xrow = a.gather_by_token ? x / a.k : a.exp2perm[x];
+            aptr[m] = a.X + (size_t)xrow * a.K + (lane >> 4) * 8;
+        }
         lds_barrier();  // the previous pass's epilogue is done with row_slot
-        if (tid < 16)
-            row_slot[tid] = x;  // for the epilogue (visible after the barriers below)
+        if (tid < kRows)
+            row_slot[tid] = a.seg_slots[beg + min(pass + tid, n_rows - 1)];
         auto load_a = [&](int vc, u32x4 (&av)[MT], bool (&am)[MT]) {
-            av[0] = load16(aptr + (kbeg + vc) * 32);  // rows past the segment: not stored
-            am[0] = true;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                if (m < n_mt) {
+                    av[m] = load16(aptr[m] + (kbeg + vc) * 32);
+                    am[m] = true;
+                }
+            }
         };
         for (int nt0 = 0; nt0 < n_nt; nt0 += NS) {
             auto load_b = [&](int vc, u32x4 (&b)[NS]) { load_b_nt(nt0, vc, b); };
             f32x4 acc[MT][NS];
             zero_acc(acc);
-            run_pipeline<MT, NS, CH>(acc, nm, 1, s0, s1, first && early, load_b, load_a);
+            run_pipeline<MT, NS, CH>(acc, nm, n_mt, s0, s1, first && early, load_b, load_a);
             first = false;
 
             lds_barrier();  // the previous epilogue is done with `part`
-            store_partials<MT, NS>(part, acc, 1, wave, lane);
+            store_partials<MT, NS>(part, acc, n_mt, wave, lane);
             lds_barrier();
 
             const int groups = min(NS, n_nt - nt0) * 2;  // 8-wide q groups
@@ -455,10 +467,25 @@ hipError_t launch_shrink(const ShrinkArgs &a, hipStream_t s)
     const int blocks = a.L * a.E_l;
     if (blocks <= 0 || a.r <= 0)
         return hipSuccess;
-    if (a.r <= 16)
-        hipLaunchKernelGGL((lora_shrink_kernel<1, 8>), dim3(blocks), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((lora_shrink_kernel<4, 2>), dim3(blocks), dim3(256), 0, s, a);
+    // rows per pass from the mean rows per (adapter, expert) segment when
+    // every slot carries an adapter: one pass covers most segments
+    const int mean = (a.n_slots + blocks - 1) / blocks;
+    const int mt = mean <= 8 ? 1 : mean <= 24 ? 2 : 3;
+    if (a.r <= 16) {
+        if (mt == 1)
+            hipLaunchKernelGGL((lora_shrink_kernel<1, 8, 1>), dim3(blocks), dim3(256), 0, s, a);
+        else if (mt == 2)
+            hipLaunchKernelGGL((lora_shrink_kernel<1, 4, 2>), dim3(blocks), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((lora_shrink_kernel<1, 4, 3>), dim3(blocks), dim3(256), 0, s, a);
+    } else {
+        if (mt == 1)
+            hipLaunchKernelGGL((lora_shrink_kernel<4, 2, 1>), dim3(blocks), dim3(256), 0, s, a);
+        else if (mt == 2)
+            hipLaunchKernelGGL((lora_shrink_kernel<4, 2, 2>), dim3(blocks), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((lora_shrink_kernel<4, 2, 3>), dim3(blocks), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -58,6 +58,17 @@ __device__ __forceinline__ void load_lds16(const void *g, uint32_t lds_addr)
                  : "memory", "m0");
 }
 
+// The same for data read once (expert weights): the nontemporal hint keeps
+// the weight stream from evicting the activation rows that the other column
+// slabs of the expert are about to read from L2.
+__device__ __forceinline__ void load_lds16_stream(const void *g, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                 :
+                 : "s"(lds_addr), "v"(g)
+                 : "memory", "m0");
+}
+
 // Physical 16-byte quarter of logical quarter q of activation row `row`.
 __device__ __forceinline__ int a_swizzle(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 
@@ -183,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_wide_kernel(GemmArgs a)
                 load_lds16(a_src[i] + vc * 32, sa + (wave + 4 * i) * 1024);
 #pragma unroll
         for (int n = 0; n < 2; ++n)
-            load_lds16(b_main + ((size_t)vc * 4 + n) * 512, sb + (2 * wave + n) * 1024);
+            load_lds16_stream(b_main + ((size_t)vc * 4 + n) * 512, sb + (2 * wave + n) * 1024);
     };
     auto issue = [&](int vc, int st) {
         if (vc < KC) {

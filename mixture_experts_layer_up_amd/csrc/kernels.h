@@ -57,6 +57,7 @@ struct ShrinkArgs {
     int r, rp, L, E_l, k;
     const int32_t *seg_offsets, *seg_slots, *exp2perm;
     uint16_t *S;              // [n, rp], row = slot x = t * k + j
+    int n_slots;              // T * k (sizes the rows per pass)
 };
 
 // Grouped expert GEMM over one packed weight stack, with the LoRA expand

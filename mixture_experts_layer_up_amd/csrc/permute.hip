@@ -25,6 +25,7 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxKeys = 8192;   // local experts, or adapters * local experts
 constexpr int kTable = 8192;     // per-wave running offsets, waves * keys
+constexpr int kKeyCache = 16384; // slot keys kept in LDS when n fits
 
 __device__ __forceinline__ int slot_key(const PermuteArgs &a, bool by_segment, int x)
 {
@@ -47,6 +48,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a)
     __shared__ int wave_excl[kWaves];
     __shared__ int tile_excl[kWaves];
     __shared__ int tile_total;
+    __shared__ int key_cache[kKeyCache];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -67,12 +69,21 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a)
         return;
     }
 
+    // 0. every slot's key, once: into LDS when the batch fits (independent
+    // loads, so they are all in flight together), else recomputed per pass
+    const bool cached = n <= kKeyCache;
+    if (cached) {
+        for (int x = tid; x < n; x += kThreads)
+            key_cache[x] = slot_key(a, by_segment, x);
+    }
+    auto key_of = [&](int x) { return cached ? key_cache[x] : slot_key(a, by_segment, x); };
+
     // 1. histogram
     for (int i = tid; i <= NK; i += kThreads)
         hist[i] = 0;
     __syncthreads();
     for (int x = tid; x < n; x += kThreads) {
-        const int key = slot_key(a, by_segment, x);
+        const int key = key_of(x);
         if (key >= 0)
             atomicAdd(&hist[key], 1);
     }
@@ -187,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a)
         const int cb = wave * chunk;
         const int ce = min(n, cb + chunk);
         for (int x = cb + lane; x < ce; x += kWave) {
-            const int key = slot_key(a, by_segment, x);
+            const int key = key_of(x);
             if (key >= 0)
                 atomicAdd(&table[wave * NK + key], 1);
         }
@@ -210,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a)
         const unsigned long long lt = (1ull << lane) - 1ull;
         for (int base = cb; base < ce; base += kWave) {
             const int x = base + lane;
-            const int key = x < ce ? slot_key(a, by_segment, x) : -1;
+            const int key = x < ce ? key_of(x) : -1;
             unsigned long long same = __ballot(key >= 0);
             for (int b = 0; b < nbits; ++b) {
                 const bool bit = (key >> b) & 1;

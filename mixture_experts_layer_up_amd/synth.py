@@ -66,6 +66,9 @@ class LayerConfig:
     sigma_lora_b: float = 0.02
     sigma_hidden: float = 1.0
     routed_scaling_factor: float = 1.0
+    # shared-outer LoRA layout: A_gu [L, 1, r, H] and B_dn [L, 1, H, r] hold one
+    # weight set per adapter for every expert; B_gu and A_dn stay per expert
+    lora_shared_outer: bool = False
 
     def replace(self, **kw) -> "LayerConfig":
         return dataclasses.replace(self, **kw)
@@ -107,10 +110,16 @@ def make_inputs(cfg: LayerConfig, seed: Optional[int] = None) -> Dict[str, np.nd
     hidden = _normal_bf16(rng, (T, H), cfg.sigma_hidden)
     w13 = _normal_bf16(rng, (E, H, 2 * I), cfg.sigma_w)[lo:hi]
     w2 = _normal_bf16(rng, (E, I, H), cfg.sigma_w)[lo:hi]
-    a_gu = _normal_bf16(rng, (L, E, rg, H), cfg.sigma_lora_a)[:, lo:hi]
+    if cfg.lora_shared_outer:  # outer matrices: one set per adapter, not sliced
+        a_gu = _normal_bf16(rng, (L, 1, rg, H), cfg.sigma_lora_a)
+    else:
+        a_gu = _normal_bf16(rng, (L, E, rg, H), cfg.sigma_lora_a)[:, lo:hi]
     b_gu = _normal_bf16(rng, (L, E, 2 * I, rg), cfg.sigma_lora_b)[:, lo:hi]
     a_dn = _normal_bf16(rng, (L, E, rd, I), cfg.sigma_lora_a)[:, lo:hi]
-    b_dn = _normal_bf16(rng, (L, E, H, rd), cfg.sigma_lora_b)[:, lo:hi]
+    if cfg.lora_shared_outer:
+        b_dn = _normal_bf16(rng, (L, 1, H, rd), cfg.sigma_lora_b)
+    else:
+        b_dn = _normal_bf16(rng, (L, E, H, rd), cfg.sigma_lora_b)[:, lo:hi]
 
     if cfg.mapping == "uniform":
         mapping = rng.integers(-1, L, size=T, dtype=np.int64).astype(np.int32)

@@ -210,6 +210,16 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
  * Slots are summed in ascending j.  A token with no local slot gets a zero
  * row.  `tokens` (length n_out) selects which rows to compute; NULL means
  * all T tokens in order.  `out` is [n_out, H].
+ *
+ * shared_outer != 0 selects the shared-outer LoRA layout ("BF16 support for
+ * the experimental_sgl_trtllm MoE-LoRA path", Flow section 2): the outer
+ * matrices hold one weight set per adapter, A_gu [L, 1, r, H] and
+ * B_dn [L, 1, H, r], addressed by the adapter alone for every expert; the
+ * inner ones, B_gu and A_dn, stay per (adapter, expert).
+ *
+ * slot_out, when not NULL, receives each slot's y (before the routing weight
+ * and the scaling factor) as [T * k, H] rows in slot order x = t * k + j, for
+ * the selected tokens; slots of other shards get zero rows.
  */
 int oracle_forward(int T, int H, int I, int E, int k, int off, int E_l,
                    int L, int r_gu, int r_dn, double routed_scaling_factor,
@@ -218,7 +228,8 @@ int oracle_forward(int T, int H, int I, int E, int k, int off, int E_l,
                    const uint16_t *w2, const uint16_t *a_gu,
                    const uint16_t *b_gu, const uint16_t *a_dn,
                    const uint16_t *b_dn, const int32_t *mapping,
-                   const int32_t *tokens, int n_out, double *out)
+                   const int32_t *tokens, int n_out, double *out,
+                   int shared_outer, double *slot_out)
 {
     (void)E;
     if (T < 0 || H <= 0 || I <= 0 || k <= 0 || E_l <= 0 || L < 0 || r_gu < 0 || r_dn < 0)
@@ -255,6 +266,10 @@ int oracle_forward(int T, int H, int I, int E, int k, int off, int E_l,
 
                 for (int j = 0; j < k; ++j) {
                     const int id = topk_ids[(size_t)t * k + j];
+                    double *yslot = slot_out ? slot_out + ((size_t)t * k + j) * H : NULL;
+                    if (yslot)
+                        for (int n = 0; n < H; ++n)
+                            yslot[n] = 0.0;
                     if (!(id >= off && id < off + E_l))
                         continue; /* expert-parallel slot owned by another shard */
                     const int e = id - off;
@@ -272,7 +287,8 @@ int oracle_forward(int T, int H, int I, int E, int k, int off, int E_l,
                     /* gate_up LoRA: shrink with A_gu [r, H], expand with B_gu [2I, r] */
                     if (l >= 0 && r_gu > 0) {
                         const size_t le = (size_t)l * E_l + e;
-                        const uint16_t *A = a_gu + le * r_gu * H;
+                        const size_t outer = shared_outer ? (size_t)l : le;
+                        const uint16_t *A = a_gu + outer * r_gu * H;
                         const uint16_t *B = b_gu + le * two_i * r_gu;
                         for (int q = 0; q < r_gu; ++q) {
                             double v = 0.0;
@@ -304,8 +320,9 @@ int oracle_forward(int T, int H, int I, int E, int k, int off, int E_l,
                     /* down LoRA: shrink with A_dn [r, I], expand with B_dn [H, r] */
                     if (l >= 0 && r_dn > 0) {
                         const size_t le = (size_t)l * E_l + e;
+                        const size_t outer = shared_outer ? (size_t)l : le;
                         const uint16_t *A = a_dn + le * r_dn * I;
-                        const uint16_t *B = b_dn + le * (size_t)H * r_dn;
+                        const uint16_t *B = b_dn + outer * (size_t)H * r_dn;
                         for (int q = 0; q < r_dn; ++q) {
                             double v = 0.0;
                             for (int i = 0; i < I; ++i)
@@ -319,6 +336,9 @@ int oracle_forward(int T, int H, int I, int E, int k, int off, int E_l,
                             y[n] += v;
                         }
                     }
+                    if (yslot)
+                        for (int n = 0; n < H; ++n)
+                            yslot[n] = y[n];
                     /* finalize: routing-weighted sum over the token's slots */
                     const double w = topk_weights[(size_t)t * k + j];
                     for (int n = 0; n < H; ++n)

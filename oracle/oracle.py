@@ -44,7 +44,7 @@ def _load():
         lib.oracle_route.restype = i32
         lib.oracle_permute.argtypes = [i32] * 6 + [vp] * 8
         lib.oracle_permute.restype = i32
-        lib.oracle_forward.argtypes = [i32] * 10 + [f64] + [vp] * 11 + [i32, vp]
+        lib.oracle_forward.argtypes = [i32] * 10 + [f64] + [vp] * 11 + [i32, vp, i32, vp]
         lib.oracle_forward.restype = i32
         _lib = lib
     return _lib
@@ -98,14 +98,18 @@ def permute(topk_ids: np.ndarray, mapping: Optional[np.ndarray], num_experts: in
 
 def forward(cfg, inputs: Dict[str, np.ndarray], topk_ids: Optional[np.ndarray] = None,
             topk_weights: Optional[np.ndarray] = None,
-            tokens: Optional[np.ndarray] = None) -> np.ndarray:
+            tokens: Optional[np.ndarray] = None, slot_outputs: bool = False):
     """fp64 layer output [n_out, H].
 
     ``cfg`` supplies the shape (``num_tokens, hidden, inter, num_experts,
     top_k, local_expert_offset, local_num_experts, num_loras, rank_gate_up,
-    rank_down, routed_scaling_factor``).  Routing comes from ``topk_ids`` /
+    rank_down, routed_scaling_factor``, and ``lora_shared_outer`` for the
+    shared-outer LoRA layout).  Routing comes from ``topk_ids`` /
     ``topk_weights`` when given, else from ``inputs['logits']`` via
-    :func:`route`.  ``tokens`` selects output rows (default: all).
+    :func:`route`.  ``tokens`` selects output rows (default: all).  With
+    ``slot_outputs`` the result is ``(out, y)``, ``y`` [T * k, H] holding each
+    slot's expert output before the routing weight (zero rows for slots of
+    other shards and for unselected tokens).
     """
     T, H, I = cfg.num_tokens, cfg.hidden, cfg.inter
     k = cfg.top_k
@@ -131,16 +135,19 @@ def forward(cfg, inputs: Dict[str, np.ndarray], topk_ids: Optional[np.ndarray] =
     E_l = cfg.local_num_experts
     assert w13.shape == (E_l, H, 2 * I) and w2.shape == (E_l, I, H)
     L, rg, rd = cfg.num_loras, cfg.rank_gate_up, cfg.rank_down
+    shared = bool(getattr(cfg, "lora_shared_outer", False))
+    outer = 1 if shared else E_l
     if L > 0 and rg > 0:
-        assert a_gu.shape == (L, E_l, rg, H) and b_gu.shape == (L, E_l, 2 * I, rg)
+        assert a_gu.shape == (L, outer, rg, H) and b_gu.shape == (L, E_l, 2 * I, rg)
     if L > 0 and rd > 0:
-        assert a_dn.shape == (L, E_l, rd, I) and b_dn.shape == (L, E_l, H, rd)
+        assert a_dn.shape == (L, E_l, rd, I) and b_dn.shape == (L, outer, H, rd)
+    y = np.zeros((T * k, H), dtype=np.float64) if slot_outputs else None
     rc = _load().oracle_forward(
         T, H, I, cfg.num_experts, k, cfg.local_expert_offset, E_l, L, rg, rd,
         float(cfg.routed_scaling_factor),
         _ptr(hidden), _ptr(ids), _ptr(w), _ptr(w13), _ptr(w2),
         _ptr(a_gu), _ptr(b_gu), _ptr(a_dn), _ptr(b_dn), _ptr(mapping),
-        _ptr(tok), n_out, _ptr(out))
+        _ptr(tok), n_out, _ptr(out), int(shared), _ptr(y))
     if rc != 0:
         raise RuntimeError(f"oracle_forward failed ({rc})")
-    return out
+    return (out, y) if slot_outputs else out

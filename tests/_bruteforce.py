@@ -33,21 +33,28 @@ def route(logits: np.ndarray, k: int):
     return ids, w
 
 
-def forward(cfg, inp, topk_ids=None, topk_weights=None):
+def _slot_ffns(cfg, inp, topk_ids):
+    """Per (token, slot): the merged-weight expert FFN output, or None for a
+    slot of another shard.  Shared-outer stacks are broadcast over experts
+    first, so the merged weights are formed the same way in both layouts."""
     T, H, I, k = cfg.num_tokens, cfg.hidden, cfg.inter, cfg.top_k
     off, E_l, L = cfg.local_expert_offset, cfg.local_num_experts, cfg.num_loras
-    if topk_ids is None:
-        topk_ids, topk_weights = route(inp["logits"], k)
     x_all = f64(inp["hidden"])
     w13, w2 = f64(inp["w13"]), f64(inp["w2"])
     has_gu = L > 0 and cfg.rank_gate_up > 0
     has_dn = L > 0 and cfg.rank_down > 0
-    a_gu = f64(inp["a_gu"]) if has_gu else None
+    shared = getattr(cfg, "lora_shared_outer", False)
+
+    def per_expert(name):
+        a = f64(inp[name])
+        return np.broadcast_to(a, (a.shape[0], E_l) + a.shape[2:]) if shared else a
+
+    a_gu = per_expert("a_gu") if has_gu else None
     b_gu = f64(inp["b_gu"]) if has_gu else None
     a_dn = f64(inp["a_dn"]) if has_dn else None
-    b_dn = f64(inp["b_dn"]) if has_dn else None
+    b_dn = per_expert("b_dn") if has_dn else None
     mapping = inp.get("mapping")
-    out = np.zeros((T, H), dtype=np.float64)
+    res = {}
     for t in range(T):
         l = -1 if mapping is None else int(mapping[t])
         if not (0 <= l < L):
@@ -55,6 +62,7 @@ def forward(cfg, inp, topk_ids=None, topk_weights=None):
         for j in range(k):
             e = int(topk_ids[t, j]) - off
             if not (0 <= e < E_l):
+                res[(t, j)] = None
                 continue
             W13 = w13[e].copy()
             W2 = w2[e].copy()
@@ -64,6 +72,27 @@ def forward(cfg, inp, topk_ids=None, topk_weights=None):
                 W2 += (b_dn[l, e] @ a_dn[l, e]).T
             h = x_all[t] @ W13
             g, u = h[:I], h[I:]
-            a = g * expit(g) * u
-            out[t] += float(topk_weights[t, j]) * (a @ W2)
+            res[(t, j)] = (g * expit(g) * u) @ W2
+    return res
+
+
+def slot_outputs(cfg, inp, topk_ids):
+    """[T * k, H]: each slot's expert output before the routing weight (zero
+    rows for slots of other shards)."""
+    T, H, k = cfg.num_tokens, cfg.hidden, cfg.top_k
+    y = np.zeros((T * k, H), dtype=np.float64)
+    for (t, j), v in _slot_ffns(cfg, inp, topk_ids).items():
+        if v is not None:
+            y[t * k + j] = v
+    return y
+
+
+def forward(cfg, inp, topk_ids=None, topk_weights=None):
+    T, H, k = cfg.num_tokens, cfg.hidden, cfg.top_k
+    if topk_ids is None:
+        topk_ids, topk_weights = route(inp["logits"], k)
+    out = np.zeros((T, H), dtype=np.float64)
+    for (t, j), v in sorted(_slot_ffns(cfg, inp, topk_ids).items()):
+        if v is not None:
+            out[t] += float(topk_weights[t, j]) * v
     return out * cfg.routed_scaling_factor

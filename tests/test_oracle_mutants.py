@@ -17,8 +17,9 @@ import pytest
 from mixture_experts_layer_up_amd.synth import make_inputs
 from oracle import oracle
 from tests import _bruteforce as bf
-from tests.test_oracle_pins import (GOLDEN, MINI_C3, MINI_EP, MINI_R16, _amplified,
-                                    _golden_cfg, _golden_inputs, _numpy_permute)
+from tests.test_oracle_pins import (GOLDEN, MINI_C3, MINI_EP, MINI_EP_SHARED, MINI_R16,
+                                    MINI_SHARED, _amplified, _golden_cfg, _golden_inputs,
+                                    _numpy_permute)
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "moe_lora_oracle.c")
 
@@ -52,6 +53,11 @@ MUTANTS = [
      "int s = (id - off) * L + l;", 0),
     ("hidden_row_wrong", "x[c] = bf16_to_double(hidden[(size_t)t * H + c]);",
      "x[c] = bf16_to_double(hidden[(size_t)((t + 1) % T) * H + c]);", 0),
+    ("shared_outer_a_first_adapter", "const size_t outer = shared_outer ? (size_t)l : le;",
+     "const size_t outer = shared_outer ? (size_t)0 : le;", 0),
+    ("shared_outer_b_first_adapter", "const size_t outer = shared_outer ? (size_t)l : le;",
+     "const size_t outer = shared_outer ? (size_t)0 : le;", 1),
+    ("slot_output_scaled", "yslot[n] = y[n];", "yslot[n] = 0.5 * y[n];", 0),
 ]
 
 
@@ -98,6 +104,19 @@ def _battery_passes() -> bool:
                                               "lora_seg_offsets", "lora_seg_slots")], ref_p):
                 if not np.array_equal(a, b):
                     return False
+        for cfg in (MINI_SHARED, MINI_EP_SHARED):
+            inp = make_inputs(cfg)
+            out = oracle.forward(cfg, inp)
+            ref = bf.forward(cfg, inp)
+            if not np.abs(out - ref).max() <= 1e-10 * np.abs(ref).max():
+                return False
+        cfg = _amplified(MINI_EP)
+        inp = make_inputs(cfg)
+        ids, w = bf.route(inp["logits"], cfg.top_k)
+        _, y = oracle.forward(cfg, inp, topk_ids=ids, topk_weights=w, slot_outputs=True)
+        y_ref = bf.slot_outputs(cfg, inp, ids)
+        if not np.abs(y - y_ref).max() <= 1e-10 * np.abs(y_ref).max():
+            return False
         with open(os.path.join(GOLDEN, "hand_worked_layer.json")) as f:
             g = json.load(f)
         if oracle.forward(_golden_cfg(g), _golden_inputs(g)).tolist() != \

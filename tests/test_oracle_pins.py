@@ -25,6 +25,11 @@ MINI_EP = LayerConfig("mini_ep", 12, 64, 32, 16, 4, 4, 8, 3, 8, 4, seed=12,
                       mapping="uniform")
 MINI_R16 = LayerConfig("mini_r16", 6, 96, 48, 8, 3, 0, 8, 2, 16, 16, seed=13,
                        mapping="uniform", sigma_lora_a=0.2, sigma_lora_b=0.2)
+# shared-outer LoRA layout (A_gu and B_dn one set per adapter), full and EP shard
+MINI_SHARED = MINI_C3.replace(name="mini_shared", lora_shared_outer=True, seed=14,
+                              sigma_lora_a=0.2, sigma_lora_b=0.2)
+MINI_EP_SHARED = MINI_EP.replace(name="mini_ep_shared", lora_shared_outer=True, seed=15,
+                                 sigma_lora_a=0.2, sigma_lora_b=0.2)
 
 
 def _amplified(cfg):
@@ -327,3 +332,53 @@ def test_hand_worked_layer():
     inp_ep = _golden_inputs(g, ep["local_expert_offset"], ep["local_num_experts"])
     out_ep = oracle.forward(cfg_ep, inp_ep)
     assert out_ep.tolist() == np.asarray(ep["expected_out"], dtype=np.float64).tolist()
+
+
+# --------------------------------------------------------------------------
+# shared-outer LoRA layout ("BF16 support for the experimental_sgl_trtllm
+# MoE-LoRA path", Flow section 2) and per-slot expert outputs
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", [MINI_SHARED, MINI_EP_SHARED], ids=lambda c: c.name)
+def test_shared_outer_matches_merged_bruteforce(cfg):
+    inp = make_inputs(cfg)
+    assert inp["a_gu"].shape[1] == 1 and inp["b_dn"].shape[1] == 1
+    out = oracle.forward(cfg, inp)
+    ref = bf.forward(cfg, inp)
+    assert np.abs(out - ref).max() <= _tol(ref)
+    base_cfg = cfg.replace(num_loras=0)
+    d_ref = ref - bf.forward(base_cfg, inp)
+    assert np.abs(d_ref).max() > 1e-3 * np.abs(ref).max()
+    assert np.abs((out - oracle.forward(base_cfg, inp)) - d_ref).max() <= _tol(d_ref)
+
+
+def test_shared_outer_equals_per_expert_with_repeated_stacks():
+    # the shared layout is the per-expert layout with the outer matrices
+    # repeated over the experts: the same arithmetic, so bitwise equal
+    cfg = MINI_SHARED
+    inp = make_inputs(cfg)
+    E_l = cfg.local_num_experts
+    tiled = dict(inp)
+    tiled["a_gu"] = np.ascontiguousarray(np.repeat(inp["a_gu"], E_l, axis=1))
+    tiled["b_dn"] = np.ascontiguousarray(np.repeat(inp["b_dn"], E_l, axis=1))
+    a = oracle.forward(cfg, inp)
+    b = oracle.forward(cfg.replace(lora_shared_outer=False), tiled)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("cfg", [_amplified(MINI_C3), _amplified(MINI_EP), MINI_EP_SHARED],
+                         ids=lambda c: c.name)
+def test_slot_outputs_match_bruteforce(cfg):
+    inp = make_inputs(cfg)
+    ids, w = bf.route(inp["logits"], cfg.top_k)
+    out, y = oracle.forward(cfg, inp, topk_ids=ids, topk_weights=w, slot_outputs=True)
+    y_ref = bf.slot_outputs(cfg, inp, ids)
+    assert np.abs(y - y_ref).max() <= _tol(y_ref)
+    # slots of other shards are zero rows
+    local = ((ids >= cfg.local_expert_offset) &
+             (ids < cfg.local_expert_offset + cfg.local_num_experts)).reshape(-1)
+    assert not np.any(y[~local])
+    # the layer output is the weighted sum of the slot outputs
+    T, k, H = cfg.num_tokens, cfg.top_k, cfg.hidden
+    summed = (w.reshape(T, k, 1) * y.reshape(T, k, H)).sum(axis=1) * cfg.routed_scaling_factor
+    assert np.abs(out - summed).max() <= _tol(out)

@@ -106,13 +106,16 @@ def algorithmic_cost(cfg, ids, mapping):
     lmap = np.repeat(np.asarray(mapping), k).reshape(ids.shape)
     lvalid = local & (lmap >= 0) & (lmap < L)
     pairs = np.unique((lmap * E_l + le)[lvalid]) if L > 0 else np.zeros(0)
+    adapters = np.unique(lmap[lvalid]) if L > 0 else np.zeros(0)
     P = int(local.sum())
     P_lora = int(lvalid.sum())
     n_e, n_pairs = len(touched), len(pairs)
+    # shared-outer layout: A_gu and B_dn once per touched adapter, not per pair
+    n_outer = len(adapters) if getattr(cfg, "lora_shared_outer", False) else n_pairs
     w13_bytes = 2 * n_e * H * 2 * I
     w2_bytes = 2 * n_e * I * H
-    lora_gu = 2 * n_pairs * (rg * H + 2 * I * rg) if rg else 0
-    lora_dn = 2 * n_pairs * (rd * I + H * rd) if rd else 0
+    lora_gu = 2 * (n_outer * rg * H + n_pairs * 2 * I * rg) if rg else 0
+    lora_dn = 2 * (n_pairs * rd * I + n_outer * H * rd) if rd else 0
     io = 2 * T * H * 2 + 4 * T * E + 4 * T
     total_bytes = w13_bytes + w2_bytes + lora_gu + lora_dn + io
     flops = 2 * P * (H * 2 * I + I * H) + 2 * P_lora * (rg * (H + 2 * I) + rd * (I + H))
@@ -251,6 +254,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode64", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--lora-layout", default="per_expert", choices=("per_expert", "shared_outer"),
+                    help="LoRA stack layout (shared_outer: A_gu and B_dn one set per adapter)")
+    ap.add_argument("--finalize", default="fused", choices=("fused", "external"),
+                    help="external: the forward exports per-slot outputs and a separate "
+                         "finalize call completes the step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle baseline time budget (0 = skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -286,6 +294,8 @@ def main():
     from mixture_experts_layer_up_amd.synth import CONFIGS, make_inputs
 
     cfg = CONFIGS[args.workload]
+    if args.lora_layout == "shared_outer":
+        cfg = cfg.replace(lora_shared_outer=True)
     log(f"[bench] generating {args.workload} inputs")
     inp = make_inputs(cfg)
     torch.cuda.set_device(0)
@@ -294,9 +304,19 @@ def main():
     out = torch.empty((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
     kw = {k: v for k, v in lay.items() if k not in ("hidden", "w13_packed", "w2_packed")}
 
+    ext_routing = binding.alloc_routing(shape, "cuda") if args.finalize == "external" else None
+    expert_out = (torch.empty((cfg.num_tokens * cfg.top_k, cfg.hidden), dtype=torch.bfloat16,
+                              device="cuda") if ext_routing is not None else None)
+
     def step(events=None):
-        binding.forward(shape, lay["hidden"], lay["w13_packed"], lay["w2_packed"], out=out,
-                        workspace=ws, stage_events=events, **kw)
+        if ext_routing is None:
+            binding.forward(shape, lay["hidden"], lay["w13_packed"], lay["w2_packed"], out=out,
+                            workspace=ws, stage_events=events, **kw)
+        else:
+            binding.forward(shape, lay["hidden"], lay["w13_packed"], lay["w2_packed"],
+                            workspace=ws, stage_events=events, routing=ext_routing,
+                            expert_out=expert_out, **kw)
+            binding.finalize(shape, expert_out, ext_routing, out=out)
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 2
@@ -422,7 +442,8 @@ def main():
                    "num_experts": cfg.num_experts, "top_k": cfg.top_k,
                    "local_expert_offset": cfg.local_expert_offset,
                    "local_num_experts": cfg.local_num_experts, "num_loras": cfg.num_loras,
-                   "rank": cfg.rank_gate_up, "parallelism": "single GPU"},
+                   "rank": cfg.rank_gate_up, "lora_layout": args.lora_layout,
+                   "finalize": args.finalize, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "gemm_gate_up_swiglu",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,

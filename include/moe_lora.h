@@ -68,7 +68,15 @@ extern "C" {
  *   local_expert_offset + local_num_experts <= num_experts
  *   0 <= num_loras <= 64, num_loras * local_num_experts <= 8192
  *   0 <= rank_gate_up, rank_down <= 256
+ *   lora_shared_outer is 0 or 1 (else MOE_LORA_ERR_INVALID_ARG)
  * A LoRA projection is active when num_loras > 0 and its rank > 0.
+ *
+ * lora_shared_outer = 1 selects the shared-outer LoRA layout ("BF16 support
+ * for the experimental_sgl_trtllm MoE-LoRA path", Flow section 2): the outer
+ * matrices hold one weight set per adapter, used for every expert and never
+ * sliced by the expert-parallel window (lora_a_gate_up [L, 1, r_gu, H],
+ * lora_b_down [L, 1, H, r_dn]); the inner ones (lora_b_gate_up, lora_a_down)
+ * stay per (adapter, local expert).
  */
 typedef struct moe_lora_shape {
     int32_t num_tokens;            /* T */
@@ -82,6 +90,7 @@ typedef struct moe_lora_shape {
     int32_t rank_gate_up;          /* r_gu */
     int32_t rank_down;             /* r_dn */
     float routed_scaling_factor;   /* multiplies the routed sum (1.0 = none) */
+    int32_t lora_shared_outer;     /* 0: per-expert LoRA stacks; 1: shared-outer */
 } moe_lora_shape;
 
 /*
@@ -124,11 +133,12 @@ typedef struct moe_lora_routing {
  *                      gate, [I, 2I) up) in the packed layout written by
  *                      moe_lora_pack_weights; 16-byte aligned
  *   w2_packed          expert down weights [E_l, I, H], packed; 16-byte aligned
- *   lora_a_gate_up     bf16 [L, E_l, r_gu, H]   (shrink, 16-byte aligned)
+ *   lora_a_gate_up     bf16 [L, E_l, r_gu, H]   (shrink, 16-byte aligned;
+ *                      [L, 1, r_gu, H] in the shared-outer layout)
  *   lora_b_gate_up     bf16 [L, E_l, 2I, r_gu]  (expand; 16-byte aligned
  *                      when r_gu % 8 == 0, else 2-byte)
  *   lora_a_down        bf16 [L, E_l, r_dn, I]
- *   lora_b_down        bf16 [L, E_l, H, r_dn]
+ *   lora_b_down        bf16 [L, E_l, H, r_dn]   ([L, 1, H, r_dn] shared-outer)
  *   token_lora_mapping int32 [T], adapter of each token, -1 = none; NULL
  *                      means every token is -1
  *   stage_events       NULL, or MOE_LORA_NUM_STAGE_EVENTS hipEvent_t handles
@@ -137,6 +147,17 @@ typedef struct moe_lora_routing {
  *                      their event recorded; a NULL entry is skipped (each
  *                      recorded event costs a few microseconds of stream
  *                      time, so record only the boundaries you need)
+ *   expert_out         NULL (finalize into `out`), or bf16 [T*k, H], 16-byte
+ *                      aligned: receives each local slot's expert output
+ *                      (down projection plus down-LoRA delta, before the
+ *                      routing weight) at its permuted row p; rows [P, T*k)
+ *                      are not written.  The finalize is then skipped (the
+ *                      pages' op likewise returns this triple instead of
+ *                      finalizing when asked: "BF16 support for the
+ *                      experimental_sgl_trtllm MoE-LoRA path", "Files
+ *                      changed" table, launcher row); moe_lora_finalize
+ *                      completes it.  Needs `routing`, which holds the other
+ *                      two members of the triple.
  * LoRA pointers may be NULL when the projection is inactive.
  */
 typedef struct moe_lora_inputs {
@@ -152,6 +173,7 @@ typedef struct moe_lora_inputs {
     const void *lora_b_down;
     const int32_t *token_lora_mapping;
     void *const *stage_events;
+    void *expert_out;
 } moe_lora_inputs;
 
 /* Bytes of device workspace moe_lora_forward needs for `shape` (host only,
@@ -193,7 +215,8 @@ int moe_lora_route(const moe_lora_shape *shape, const float *router_logits,
                    void *stream);
 
 /*
- * The layer forward.  Writes `out` bf16 [T, H] (16-byte aligned) completely:
+ * The layer forward.  Writes `out` bf16 [T, H] (16-byte aligned; NULL when
+ * inputs->expert_out is set) completely:
  * rows of tokens with no local slot are 0, so `out` needs no clearing.  With
  * several expert-parallel shards, `out` is this shard's partial sum.
  * `routing` is NULL, or receives the routing arrays as moe_lora_route
@@ -205,6 +228,21 @@ int moe_lora_route(const moe_lora_shape *shape, const float *router_logits,
 int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *inputs,
                      const moe_lora_routing *routing, void *out, void *workspace,
                      size_t workspace_bytes, void *stream);
+
+/*
+ * The finalize on its own ("BF16 support for the experimental_sgl_trtllm
+ * MoE-LoRA path", "Files changed" table, launcher row: routing-weighted sum
+ * of each token's slot outputs): out[t] = routed_scaling_factor *
+ * sum_j topk_weights[t, j] * expert_out[expanded_idx_to_permuted_idx[t*k+j]]
+ * over the slots whose permuted index is not -1, in ascending j, fp32 sum,
+ * one bf16 rounding; rows of tokens without a local slot are 0.  With the
+ * arrays a moe_lora_forward call exported (expert_out set), the result is
+ * bitwise the `out` that call would have written without expert_out.
+ * expert_out bf16 [T*k, H] and out bf16 [T, H] 16-byte aligned, device.
+ */
+int moe_lora_finalize(const moe_lora_shape *shape, const void *expert_out,
+                      const int32_t *expanded_idx_to_permuted_idx, const float *topk_weights,
+                      void *out, void *stream);
 
 /* Static description of a status code. */
 const char *moe_lora_strerror(int status);

@@ -35,6 +35,7 @@ class Shape(ctypes.Structure):
         ("rank_gate_up", ctypes.c_int32),
         ("rank_down", ctypes.c_int32),
         ("routed_scaling_factor", ctypes.c_float),
+        ("lora_shared_outer", ctypes.c_int32),
     ]
 
 
@@ -49,7 +50,7 @@ class Inputs(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in (
         "hidden", "router_logits", "topk_ids", "topk_weights", "w13_packed", "w2_packed",
         "lora_a_gate_up", "lora_b_gate_up", "lora_a_down", "lora_b_down",
-        "token_lora_mapping", "stage_events")]
+        "token_lora_mapping", "stage_events", "expert_out")]
 
 
 NUM_STAGE_EVENTS = 7
@@ -85,6 +86,8 @@ def load_library(path: str = LIB_PATH):
     lib.moe_lora_route.restype = ctypes.c_int
     lib.moe_lora_forward.argtypes = [P(Shape), P(Inputs), P(Routing), vp, vp, ctypes.c_size_t, vp]
     lib.moe_lora_forward.restype = ctypes.c_int
+    lib.moe_lora_finalize.argtypes = [P(Shape), vp, vp, vp, vp, vp]
+    lib.moe_lora_finalize.restype = ctypes.c_int
     lib.moe_lora_strerror.argtypes = [ctypes.c_int]
     lib.moe_lora_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -101,7 +104,8 @@ def header_functions(path: str = HEADER_PATH):
 def make_shape(cfg) -> Shape:
     return Shape(cfg.num_tokens, cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k,
                  cfg.local_expert_offset, cfg.local_num_experts, cfg.num_loras,
-                 cfg.rank_gate_up, cfg.rank_down, float(cfg.routed_scaling_factor))
+                 cfg.rank_gate_up, cfg.rank_down, float(cfg.routed_scaling_factor),
+                 int(bool(getattr(cfg, "lora_shared_outer", False))))
 
 
 def _check(rc: int):
@@ -191,11 +195,18 @@ def forward(shape: Shape, hidden: torch.Tensor, w13_packed: torch.Tensor,
             router_logits=None, topk_ids=None, topk_weights=None,
             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
             routing: Optional[Dict[str, torch.Tensor]] = None,
-            stage_events: Optional[Sequence[int]] = None) -> torch.Tensor:
-    """One layer forward on the current stream; returns ``out`` bf16 [T, H]."""
+            stage_events: Optional[Sequence[int]] = None,
+            expert_out: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
+    """One layer forward on the current stream; returns ``out`` bf16 [T, H].
+
+    With ``expert_out`` (bf16 [T*k, H]) the per-slot expert outputs are
+    written there at their permuted rows and the finalize is skipped (returns
+    None; needs ``routing``); :func:`finalize` completes it.
+    """
     T, H, I, E, k = shape.num_tokens, shape.hidden, shape.inter, shape.num_experts, shape.top_k
     E_l, L, rg, rd = shape.local_num_experts, shape.num_loras, shape.rank_gate_up, shape.rank_down
-    if out is None:
+    outer = 1 if shape.lora_shared_outer else E_l
+    if out is None and expert_out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=hidden.device)
     ws_bytes = workspace_size(shape)
     if workspace is None:
@@ -214,18 +225,38 @@ def forward(shape: Shape, hidden: torch.Tensor, w13_packed: torch.Tensor,
         _ptr(topk_weights, torch.float32, (T, k), "topk_weights"),
         _ptr(w13_packed, _BF16, (E_l, H, 2 * I), "w13_packed"),
         _ptr(w2_packed, _BF16, (E_l, I, H), "w2_packed"),
-        _ptr(lora_a_gate_up, _BF16, (L, E_l, rg, H), "lora_a_gate_up") if gu else None,
+        _ptr(lora_a_gate_up, _BF16, (L, outer, rg, H), "lora_a_gate_up") if gu else None,
         _ptr(lora_b_gate_up, _BF16, (L, E_l, 2 * I, rg), "lora_b_gate_up") if gu else None,
         _ptr(lora_a_down, _BF16, (L, E_l, rd, I), "lora_a_down") if dn else None,
-        _ptr(lora_b_down, _BF16, (L, E_l, H, rd), "lora_b_down") if dn else None,
+        _ptr(lora_b_down, _BF16, (L, outer, H, rd), "lora_b_down") if dn else None,
         _ptr(token_lora_mapping, torch.int32, (T,), "token_lora_mapping"),
         ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None,
+        _ptr(expert_out, _BF16, (T * k, H), "expert_out"),
     )
     rs = _routing_struct(routing) if routing is not None else None
     _check(load_library().moe_lora_forward(
         ctypes.byref(shape), ctypes.byref(inputs), ctypes.byref(rs) if rs is not None else None,
         _ptr(out, _BF16, (T, H), "out"), _ptr(workspace, None, None, "workspace"),
         workspace.numel() * workspace.element_size(), _stream()))
+    return out
+
+
+def finalize(shape: Shape, expert_out: torch.Tensor, routing: Dict[str, torch.Tensor],
+             topk_weights: Optional[torch.Tensor] = None,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The routing-weighted finalize of per-slot expert outputs (as written by
+    :func:`forward` with ``expert_out``); returns ``out`` bf16 [T, H].  The
+    weights are ``routing['topk_weights']`` unless ``topk_weights`` is given."""
+    T, H, k = shape.num_tokens, shape.hidden, shape.top_k
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=expert_out.device)
+    w = topk_weights if topk_weights is not None else routing["topk_weights"]
+    _check(load_library().moe_lora_finalize(
+        ctypes.byref(shape), _ptr(expert_out, _BF16, (T * k, H), "expert_out"),
+        _ptr(routing["expanded_idx_to_permuted_idx"], torch.int32, (T * k,),
+             "expanded_idx_to_permuted_idx"),
+        _ptr(w, torch.float32, (T, k), "topk_weights"),
+        _ptr(out, _BF16, (T, H), "out"), _stream()))
     return out
 
 

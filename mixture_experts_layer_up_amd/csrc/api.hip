@@ -54,6 +54,8 @@ int validate_shape(const moe_lora_shape *s)
         return MOE_LORA_ERR_UNSUPPORTED_SHAPE;
     if (!std::isfinite(s->routed_scaling_factor))
         return MOE_LORA_ERR_INVALID_ARG;
+    if (s->lora_shared_outer != 0 && s->lora_shared_outer != 1)
+        return MOE_LORA_ERR_INVALID_ARG;
     return MOE_LORA_OK;
 }
 
@@ -261,7 +263,12 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
             MOE_TRY(record(in->stage_events, i, st));
         return MOE_LORA_OK;
     }
-    if (!out || !workspace || !in->hidden || !in->w13_packed || !in->w2_packed)
+    // expert_out: the per-slot outputs go to the caller and the finalize is
+    // skipped; the caller needs the routing export to finalize them
+    void *expert_out = in->expert_out;
+    if ((!expert_out && !out) || (expert_out && !routing))
+        return MOE_LORA_ERR_INVALID_ARG;
+    if (!workspace || !in->hidden || !in->w13_packed || !in->w2_packed)
         return MOE_LORA_ERR_INVALID_ARG;
     const bool from_logits = in->router_logits != nullptr;
     if (from_logits == (in->topk_ids != nullptr || in->topk_weights != nullptr))
@@ -275,7 +282,7 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     if (dn && (!in->lora_a_down || !in->lora_b_down))
         return MOE_LORA_ERR_INVALID_ARG;
     if (!aligned(in->hidden, 16) || !aligned(in->w13_packed, 16) || !aligned(in->w2_packed, 16) ||
-        !aligned(out, 16) || !aligned(workspace, kAlign))
+        !aligned(out, 16) || !aligned(expert_out, 16) || !aligned(workspace, kAlign))
         return MOE_LORA_ERR_MISALIGNED;
     if (gu && (!aligned(in->lora_a_gate_up, 16) ||
                !aligned(in->lora_b_gate_up, shape->rank_gate_up % 8 == 0 ? 16 : 2)))
@@ -324,7 +331,8 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     uint16_t *s_gu = reinterpret_cast<uint16_t *>(ws + lay.s_gu);
     uint16_t *act = reinterpret_cast<uint16_t *>(ws + lay.act);
     uint16_t *s_dn = reinterpret_cast<uint16_t *>(ws + lay.s_dn);
-    uint16_t *y = reinterpret_cast<uint16_t *>(ws + lay.y);
+    uint16_t *y = expert_out ? static_cast<uint16_t *>(expert_out)
+                             : reinterpret_cast<uint16_t *>(ws + lay.y);
     const uint16_t *hidden = static_cast<const uint16_t *>(in->hidden);
 
     MOE_TRY(record(ev, 0, st));
@@ -338,7 +346,7 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     if (gu) {
         ShrinkArgs sa{hidden, 1, H, static_cast<const uint16_t *>(in->lora_a_gate_up),
                       rg, round8(rg), L, E_l, k, r.seg_offsets, r.seg_slots, r.exp2perm, s_gu,
-                      T * k};
+                      T * k, shape->lora_shared_outer};
         MOE_TRY(check(launch_shrink(sa, st)));
     }
     MOE_TRY(record(ev, 2, st));
@@ -375,7 +383,7 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     if (dn) {
         ShrinkArgs sa{act, 0, I, static_cast<const uint16_t *>(in->lora_a_down),
                       rd, round8(rd), L, E_l, k, r.seg_offsets, r.seg_slots, r.exp2perm, s_dn,
-                      T * k};
+                      T * k, 0};
         MOE_TRY(check(launch_shrink(sa, st)));
     }
     MOE_TRY(record(ev, 4, st));
@@ -404,14 +412,34 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     g2.Y = y;
     g2.n_slabs = slabs(g2.NT);
     g2.zeros = static_cast<const uint16_t *>(zeros);
+    g2.lb_shared = shape->lora_shared_outer;
     MOE_TRY(check(launch_gemm_down(g2, st)));
     MOE_TRY(record(ev, 5, st));
 
-    FinalizeArgs fa{y, r.exp2perm, weights, static_cast<uint16_t *>(out), T, H, k,
-                    shape->routed_scaling_factor};
-    MOE_TRY(check(launch_finalize(fa, st)));
+    if (!expert_out) {
+        FinalizeArgs fa{y, r.exp2perm, weights, static_cast<uint16_t *>(out), T, H, k,
+                        shape->routed_scaling_factor};
+        MOE_TRY(check(launch_finalize(fa, st)));
+    }
     MOE_TRY(record(ev, 6, st));
     return MOE_LORA_OK;
+}
+
+int moe_lora_finalize(const moe_lora_shape *shape, const void *expert_out,
+                      const int32_t *expanded_idx_to_permuted_idx, const float *topk_weights,
+                      void *out, void *stream)
+{
+    MOE_TRY(validate_shape(shape));
+    if (shape->num_tokens == 0)
+        return MOE_LORA_OK;
+    if (!expert_out || !expanded_idx_to_permuted_idx || !topk_weights || !out)
+        return MOE_LORA_ERR_INVALID_ARG;
+    if (!aligned(expert_out, 16) || !aligned(out, 16))
+        return MOE_LORA_ERR_MISALIGNED;
+    FinalizeArgs fa{static_cast<const uint16_t *>(expert_out), expanded_idx_to_permuted_idx,
+                    topk_weights, static_cast<uint16_t *>(out), shape->num_tokens,
+                    shape->hidden, shape->top_k, shape->routed_scaling_factor};
+    return check(launch_finalize(fa, static_cast<hipStream_t>(stream)));
 }
 
 const char *moe_lora_strerror(int status)

@@ -215,7 +215,8 @@ __global__ __launch_bounds__(256, MT == 1 ? (kRank8 ? MOE_LORA_DECODE_WAVES : 3)
             const uint16_t *pm = wbase + ((size_t)kc * NS + n) * 512;
             const int col = kGated ? (n & 1) * a.I + (slab * 2 + (n >> 1)) * 16 + (lane & 15)
                                    : (slab * NS + n) * 16 + (lane & 15);
-            const uint16_t *pe = lb + (((size_t)aid_c * a.E_l + le) * a.n_canon + col) * a.r;
+            const size_t stack = a.lb_shared ? (size_t)aid_c : (size_t)aid_c * a.E_l + le;
+            const uint16_t *pe = lb + (stack * a.n_canon + col) * a.r;
             if (kRank8) {
                 // past the last adapter (aid >= L) the clamped stack is read; its
                 // K positions meet zero activations, so it adds nothing
@@ -345,7 +346,8 @@ __global__ __launch_bounds__(256, 2) void lora_shrink_kernel(ShrinkArgs a)
     const int kbeg = min(KC, wave * kc_per);
     const int nm = min(KC, kbeg + kc_per) - kbeg;
     const int n_nt = (a.r + 15) >> 4;
-    const uint16_t *abase = a.A + (size_t)seg * a.r * a.K + (lane >> 4) * 8;
+    const int stack = a.a_shared ? seg / a.E_l : seg;  // shared: one stack per adapter
+    const uint16_t *abase = a.A + (size_t)stack * a.r * a.K + (lane >> 4) * 8;
 
     Stage<MT, NS, CH> s0, s1;
     auto load_b_nt = [&](int nt0, int vc, u32x4 (&b)[NS]) {

@@ -220,7 +220,8 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_wide_kernel(GemmArgs a)
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             const uint16_t *p =
-                aid < a.L ? a.LB + (((size_t)aid * a.E_l + le) * a.n_canon + b_col[n]) * a.r + q0
+                aid < a.L ? a.LB + (((a.lb_shared ? (size_t)aid : (size_t)aid * a.E_l + le) *
+                                         a.n_canon + b_col[n]) * a.r + q0)
                           : zeros;
             load_lds16(p, sb + (2 * wave + n) * 1024);
         }

@@ -58,6 +58,7 @@ struct ShrinkArgs {
     const int32_t *seg_offsets, *seg_slots, *exp2perm;
     uint16_t *S;              // [n, rp], row = slot x = t * k + j
     int n_slots;              // T * k (sizes the rows per pass)
+    int a_shared;             // A holds one stack per adapter ([L, 1, r, K])
 };
 
 // Grouped expert GEMM over one packed weight stack, with the LoRA expand
@@ -80,6 +81,7 @@ struct GemmArgs {
     uint16_t *Y;              // gated: act [n, I]; else y [n, n_canon]
     int n_slabs;
     const uint16_t *zeros;    // kZeroBytes of zeros
+    int lb_shared;            // LB holds one stack per adapter ([L, 1, n_canon, r])
 };
 
 // Rows per GEMM work-list tile: 16 for the decode-shaped kernel (few rows

@@ -76,7 +76,7 @@ def _inputs(**over):
     base = dict(hidden=_fake(), router_logits=_fake(), topk_ids=None, topk_weights=None,
                 w13_packed=_fake(), w2_packed=_fake(), lora_a_gate_up=_fake(),
                 lora_b_gate_up=_fake(), lora_a_down=_fake(), lora_b_down=_fake(),
-                token_lora_mapping=_fake(), stage_events=None)
+                token_lora_mapping=_fake(), stage_events=None, expert_out=None)
     base.update(over)
     return binding.Inputs(*[base[n] for n, _ in binding.Inputs._fields_])
 
@@ -90,6 +90,7 @@ def _inputs(**over):
     (dict(w2_packed=None), ERR_INVALID_ARG),
     (dict(hidden=_fake(4096 + 8)), ERR_ALIGN),
     (dict(lora_a_gate_up=_fake(4096 + 2)), ERR_ALIGN),
+    (dict(expert_out=_fake()), ERR_INVALID_ARG),                         # no routing export
 ])
 def test_forward_argument_validation(lib, over, expect):
     shape = binding.make_shape(CONFIGS["decode64"])
@@ -136,3 +137,51 @@ def test_route_and_pack_validation(lib):
                                      _fake(), None) == ERR_ALIGN
     assert lib.moe_lora_packed_w13_bytes(ctypes.byref(shape)) == 8 * 128 * 128 * 2
     assert lib.moe_lora_packed_w2_bytes(ctypes.byref(shape)) == 8 * 64 * 128 * 2
+
+
+def _routing_fake():
+    return binding.Routing(*[_fake(8192 * (i + 1)) for i in range(len(binding.Routing._fields_))])
+
+
+def test_expert_out_mode_validation(lib):
+    shape = binding.make_shape(CONFIGS["decode64"])
+    ws = binding.workspace_size(shape)
+    rs = _routing_fake()
+    # per-slot outputs instead of `out`: out may be NULL; validation then reaches
+    # the workspace check (too small, so nothing is launched)
+    inp = _inputs(expert_out=_fake(1 << 22))
+    assert lib.moe_lora_forward(ctypes.byref(shape), ctypes.byref(inp), ctypes.byref(rs), None,
+                                _fake(1 << 20), ws - 1, None) == ERR_WS
+    inp = _inputs(expert_out=_fake((1 << 22) + 8))
+    assert lib.moe_lora_forward(ctypes.byref(shape), ctypes.byref(inp), ctypes.byref(rs), None,
+                                _fake(1 << 20), ws, None) == ERR_ALIGN
+    # neither out nor expert_out
+    inp = _inputs()
+    assert lib.moe_lora_forward(ctypes.byref(shape), ctypes.byref(inp), ctypes.byref(rs), None,
+                                _fake(1 << 20), ws, None) == ERR_INVALID_ARG
+
+
+def test_finalize_validation(lib):
+    shape = binding.make_shape(CONFIGS["decode64"])
+    assert lib.moe_lora_finalize(ctypes.byref(shape), None, _fake(), _fake(), _fake(),
+                                 None) == ERR_INVALID_ARG
+    assert lib.moe_lora_finalize(ctypes.byref(shape), _fake(), _fake(), _fake(), None,
+                                 None) == ERR_INVALID_ARG
+    assert lib.moe_lora_finalize(ctypes.byref(shape), _fake(4096 + 4), _fake(), _fake(),
+                                 _fake(), None) == ERR_ALIGN
+    assert lib.moe_lora_finalize(None, _fake(), _fake(), _fake(), _fake(),
+                                 None) == ERR_INVALID_ARG
+    empty = binding.make_shape(CONFIGS["decode64"].replace(num_tokens=0))
+    assert lib.moe_lora_finalize(ctypes.byref(empty), None, None, None, None, None) == 0
+
+
+def test_shared_outer_flag_validation(lib):
+    cfg = CONFIGS["decode64"].replace(lora_shared_outer=True)
+    shape = binding.make_shape(cfg)
+    assert shape.lora_shared_outer == 1
+    assert binding.workspace_size(shape) > 0
+    shape.lora_shared_outer = 2
+    assert binding.workspace_size(shape) == 0
+    inp = _inputs()
+    assert lib.moe_lora_forward(ctypes.byref(shape), ctypes.byref(inp), None, _fake(),
+                                _fake(1 << 20), 1 << 30, None) == ERR_INVALID_ARG

@@ -51,18 +51,18 @@ class HipEvents:
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
                                                  ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
-    def create(self, n: int):
+    def create(self, n: int, disable_timing: bool = False):
         out = []
         for _ in range(n):
             ev = ctypes.c_void_p()
-            rc = self.hip.hipEventCreate(ctypes.byref(ev))
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(ev), 2 if disable_timing else 0)
             if rc != 0:
                 raise RuntimeError(f"hipEventCreate failed ({rc})")
             out.append(ev.value)
@@ -259,6 +259,9 @@ def main():
     ap.add_argument("--finalize", default="fused", choices=("fused", "external"),
                     help="external: the forward exports per-slot outputs and a separate "
                          "finalize call completes the step")
+    ap.add_argument("--two-stream", type=int, default=0,
+                    help="1: gate_up LoRA shrink on a second stream, concurrent with the "
+                         "main-K part of the gate_up GEMM")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle baseline time budget (0 = skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -304,6 +307,11 @@ def main():
     out = torch.empty((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
     kw = {k: v for k, v in lay.items() if k not in ("hidden", "w13_packed", "w2_packed")}
 
+    if args.two_stream:
+        side_stream = torch.cuda.Stream()   # default priority
+        hip_side = HipEvents()
+        fork_ev, join_ev = hip_side.create(2, disable_timing=True)
+        kw.update(side_stream=side_stream.cuda_stream, fork_event=fork_ev, join_event=join_ev)
     ext_routing = binding.alloc_routing(shape, "cuda") if args.finalize == "external" else None
     expert_out = (torch.empty((cfg.num_tokens * cfg.top_k, cfg.hidden), dtype=torch.bfloat16,
                               device="cuda") if ext_routing is not None else None)
@@ -443,7 +451,8 @@ def main():
                    "local_expert_offset": cfg.local_expert_offset,
                    "local_num_experts": cfg.local_num_experts, "num_loras": cfg.num_loras,
                    "rank": cfg.rank_gate_up, "lora_layout": args.lora_layout,
-                   "finalize": args.finalize, "parallelism": "single GPU"},
+                   "finalize": args.finalize, "two_stream": bool(args.two_stream),
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "gemm_gate_up_swiglu",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,

@@ -158,6 +158,23 @@ typedef struct moe_lora_routing {
  *                      changed" table, launcher row); moe_lora_finalize
  *                      completes it.  Needs `routing`, which holds the other
  *                      two members of the triple.
+ *   side_stream        NULL (everything on `stream`), or a second hipStream_t
+ *                      (default priority) for the gate_up LoRA shrink, which
+ *                      then runs concurrently with the main-K part of the
+ *                      gate_up GEMM (the pages' two-stream schedule: "BF16
+ *                      support for the experimental_sgl_trtllm MoE-LoRA
+ *                      path", Summary (phase 2) and Flow section 1(B)).  The
+ *                      GEMM is then split in two launches joined by an fp32
+ *                      pre-activation in the workspace: results equal the
+ *                      one-stream ones within rounding, not bitwise.
+ *   fork_event,        caller-owned hipEvent_t handles (timing may be
+ *   join_event         disabled), required with side_stream: fork_event is
+ *                      recorded on `stream` after routing and waited by
+ *                      side_stream; join_event is recorded on side_stream
+ *                      after the shrink and waited by `stream` before the
+ *                      LoRA expand.  Nothing is allocated, so a two-stream
+ *                      forward can be captured into a HIP graph.  Ignored
+ *                      when the gate_up LoRA is inactive.
  * LoRA pointers may be NULL when the projection is inactive.
  */
 typedef struct moe_lora_inputs {
@@ -174,10 +191,15 @@ typedef struct moe_lora_inputs {
     const int32_t *token_lora_mapping;
     void *const *stage_events;
     void *expert_out;
+    void *side_stream;
+    void *fork_event;
+    void *join_event;
 } moe_lora_inputs;
 
 /* Bytes of device workspace moe_lora_forward needs for `shape` (host only,
- * pure; 0 for an invalid shape).  The workspace must be 256-byte aligned. */
+ * pure; 0 for an invalid shape), including the fp32 pre-activation
+ * [T*k, 2I] that the two-stream schedule uses.  The workspace must be
+ * 256-byte aligned. */
 size_t moe_lora_workspace_size(const moe_lora_shape *shape);
 
 /* Bytes of the packed expert weights (equal to the unpacked sizes). */

@@ -50,7 +50,8 @@ class Inputs(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in (
         "hidden", "router_logits", "topk_ids", "topk_weights", "w13_packed", "w2_packed",
         "lora_a_gate_up", "lora_b_gate_up", "lora_a_down", "lora_b_down",
-        "token_lora_mapping", "stage_events", "expert_out")]
+        "token_lora_mapping", "stage_events", "expert_out", "side_stream", "fork_event",
+        "join_event")]
 
 
 NUM_STAGE_EVENTS = 7
@@ -196,12 +197,16 @@ def forward(shape: Shape, hidden: torch.Tensor, w13_packed: torch.Tensor,
             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
             routing: Optional[Dict[str, torch.Tensor]] = None,
             stage_events: Optional[Sequence[int]] = None,
-            expert_out: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
+            expert_out: Optional[torch.Tensor] = None,
+            side_stream: Optional[int] = None, fork_event: Optional[int] = None,
+            join_event: Optional[int] = None) -> Optional[torch.Tensor]:
     """One layer forward on the current stream; returns ``out`` bf16 [T, H].
 
     With ``expert_out`` (bf16 [T*k, H]) the per-slot expert outputs are
     written there at their permuted rows and the finalize is skipped (returns
-    None; needs ``routing``); :func:`finalize` completes it.
+    None; needs ``routing``); :func:`finalize` completes it.  ``side_stream``,
+    ``fork_event``, ``join_event`` (raw hipStream_t / hipEvent_t handles)
+    select the two-stream schedule for the gate_up LoRA.
     """
     T, H, I, E, k = shape.num_tokens, shape.hidden, shape.inter, shape.num_experts, shape.top_k
     E_l, L, rg, rd = shape.local_num_experts, shape.num_loras, shape.rank_gate_up, shape.rank_down
@@ -232,6 +237,7 @@ def forward(shape: Shape, hidden: torch.Tensor, w13_packed: torch.Tensor,
         _ptr(token_lora_mapping, torch.int32, (T,), "token_lora_mapping"),
         ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None,
         _ptr(expert_out, _BF16, (T * k, H), "expert_out"),
+        side_stream, fork_event, join_event,
     )
     rs = _routing_struct(routing) if routing is not None else None
     _check(load_library().moe_lora_forward(

@@ -65,7 +65,7 @@ bool lora_down_active(const moe_lora_shape *s) { return s->num_loras > 0 && s->r
 // Workspace regions; every offset is a multiple of 256 bytes.
 struct Layout {
     size_t ids, weights, counts, offsets, exp2perm, perm2exp, seg_offsets, seg_slots;
-    size_t tiles, tile_count, zeros, s_gu, act, s_dn, y;
+    size_t tiles, tile_count, zeros, s_gu, act, s_dn, y, h;
     int tile_rows, max_tiles;
     size_t total;
 };
@@ -101,6 +101,7 @@ Layout make_layout(const moe_lora_shape *s)
     L.act = take(n * (size_t)s->inter * 2);
     L.s_dn = take(lora_down_active(s) ? n * round8(s->rank_down) * 2 : 0);
     L.y = take(n * (size_t)s->hidden * 2);
+    L.h = take(n * 2 * (size_t)s->inter * 4);  // two-stream schedule only
     L.total = o;
     return L;
 }
@@ -270,6 +271,8 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
         return MOE_LORA_ERR_INVALID_ARG;
     if (!workspace || !in->hidden || !in->w13_packed || !in->w2_packed)
         return MOE_LORA_ERR_INVALID_ARG;
+    if (in->side_stream && (!in->fork_event || !in->join_event))
+        return MOE_LORA_ERR_INVALID_ARG;
     const bool from_logits = in->router_logits != nullptr;
     if (from_logits == (in->topk_ids != nullptr || in->topk_weights != nullptr))
         return MOE_LORA_ERR_INVALID_ARG;
@@ -343,11 +346,24 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
                             tiles, lay.tile_rows, lay.max_tiles, tile_count, zeros));
     MOE_TRY(record(ev, 1, st));
 
+    // Two-stream schedule: the gate_up shrink runs on the side stream while
+    // the main-K part of the gate_up GEMM runs here; the expand waits for it.
+    const bool two_stream = gu && in->side_stream != nullptr;
+    hipStream_t side = static_cast<hipStream_t>(in->side_stream);
+    hipEvent_t fork = static_cast<hipEvent_t>(in->fork_event);
+    hipEvent_t join = static_cast<hipEvent_t>(in->join_event);
     if (gu) {
         ShrinkArgs sa{hidden, 1, H, static_cast<const uint16_t *>(in->lora_a_gate_up),
                       rg, round8(rg), L, E_l, k, r.seg_offsets, r.seg_slots, r.exp2perm, s_gu,
                       T * k, shape->lora_shared_outer};
-        MOE_TRY(check(launch_shrink(sa, st)));
+        if (two_stream) {
+            MOE_TRY(check(hipEventRecord(fork, st)));
+            MOE_TRY(check(hipStreamWaitEvent(side, fork, 0)));
+            MOE_TRY(check(launch_shrink(sa, side)));
+            MOE_TRY(check(hipEventRecord(join, side)));
+        } else {
+            MOE_TRY(check(launch_shrink(sa, st)));
+        }
     }
     MOE_TRY(record(ev, 2, st));
 
@@ -377,7 +393,16 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     auto slabs = [&](int NT) { return lay.tile_rows == kDecodeTileRows ? NT / 4 : NT / 8; };
     g1.n_slabs = slabs(g1.NT);
     g1.zeros = static_cast<const uint16_t *>(zeros);
-    MOE_TRY(check(launch_gemm_gate_up(g1, st)));
+    if (two_stream) {
+        g1.H = reinterpret_cast<float *>(ws + lay.h);
+        g1.phase = 1;
+        MOE_TRY(check(launch_gemm_gate_up(g1, st)));
+        MOE_TRY(check(hipStreamWaitEvent(st, join, 0)));
+        g1.phase = 2;
+        MOE_TRY(check(launch_gemm_gate_up(g1, st)));
+    } else {
+        MOE_TRY(check(launch_gemm_gate_up(g1, st)));
+    }
     MOE_TRY(record(ev, 3, st));
 
     if (dn) {

@@ -191,8 +191,9 @@ __global__ __launch_bounds__(256, MT == 1 ? (kRank8 ? MOE_LORA_DECODE_WAVES : 3)
     // waves take K chunks round-robin (wave w: chunks w, w + 4, ...), so the
     // block's loads at any moment cover one contiguous stretch of its slab
     const int KC = a.K >> 5;
-    const int nm = wave < KC ? (KC - wave + 3) >> 2 : 0;  // this wave's main chunks
-    const bool lora = a.S != nullptr && a.L > 0 && a.r > 0;
+    // this wave's main chunks (none in phase 2)
+    const int nm = (a.phase != 2 && wave < KC) ? (KC - wave + 3) >> 2 : 0;
+    const bool lora = a.S != nullptr && a.L > 0 && a.r > 0 && a.phase != 1;
     const int n_ext = lora ? (a.L * a.rp + 31) >> 5 : 0;
     const int ne = wave < n_ext ? (n_ext - wave + 3) >> 2 : 0;  // ext chunks wave, wave+4, ..
     const int nv = nm + ne;
@@ -285,8 +286,29 @@ __global__ __launch_bounds__(256, MT == 1 ? (kRank8 ? MOE_LORA_DECODE_WAVES : 3)
     store_partials<MT, NS>(part, acc, n_mt, wave, lane);
     __syncthreads();
 
-    if (kGated) {
-        // 32 activation columns per row: 4 groups of 8 (gate/up pair jj, half c0)
+    if (kGated && a.phase == 1) {
+        // fp32 pre-activation: 4 groups of 8 per row (gate/up pair jj, half c0)
+        for (int item = tid; item < n_rows * 4; item += 256) {
+            const int row = item >> 2;
+            const int jj = (item >> 1) & 1;
+            const int c0 = (item & 1) * 8;
+            float *hrow = a.H + (size_t)(row0 + row) * 2 * a.I + (slab * 2 + jj) * 16 + c0;
+#pragma unroll
+            for (int i = 0; i < 8; i += 4) {
+                f32x4 g, u;
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    g[h] = sum_partials<MT>(part, row, (2 * jj) * 16 + c0 + i + h);
+                    u[h] = sum_partials<MT>(part, row, (2 * jj + 1) * 16 + c0 + i + h);
+                }
+                *reinterpret_cast<f32x4 *>(hrow + i) = g;
+                *reinterpret_cast<f32x4 *>(hrow + a.I + i) = u;
+            }
+        }
+    } else if (kGated) {
+        // 32 activation columns per row: 4 groups of 8 (gate/up pair jj, half c0);
+        // in phase 2 the pre-activation of phase 1 is added first
+        const bool add_h = a.phase == 2;
         for (int item = tid; item < n_rows * 4; item += 256) {
             const int row = item >> 2;
             const int jj = (item >> 1) & 1;
@@ -297,8 +319,14 @@ __global__ __launch_bounds__(256, MT == 1 ? (kRank8 ? MOE_LORA_DECODE_WAVES : 3)
                 float v[2];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const float gate = sum_partials<MT>(part, row, (2 * jj) * 16 + c0 + i + h);
-                    const float up = sum_partials<MT>(part, row, (2 * jj + 1) * 16 + c0 + i + h);
+                    float gate = sum_partials<MT>(part, row, (2 * jj) * 16 + c0 + i + h);
+                    float up = sum_partials<MT>(part, row, (2 * jj + 1) * 16 + c0 + i + h);
+                    if (add_h) {
+                        const float *hrow = a.H + (size_t)(row0 + row) * 2 * a.I +
+                                            (slab * 2 + jj) * 16 + c0 + i + h;
+                        gate += hrow[0];
+                        up += hrow[a.I];
+                    }
                     v[h] = silu_f32(gate) * up;
                 }
                 packed[i >> 1] = float_to_bf16_bits(v[0]) | (float_to_bf16_bits(v[1]) << 16);

@@ -130,6 +130,9 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_wide_kernel(GemmArgs a)
     const bool lora = a.S != nullptr && a.L > 0 && a.r > 0;
     const int n_ext = lora ? (a.L * a.rp + 31) >> 5 : 0;
     const int nv = KC + n_ext;
+    // chunks of this launch: main K only (phase 1), expand only (phase 2), or all
+    const int vbeg = a.phase == 2 ? KC : 0;
+    const int vend = a.phase == 1 ? KC : nv;
 
     // rows of this tile: slot, source row, adapter (rows past the tile
     // repeat the last row and carry no adapter)
@@ -288,10 +291,10 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_wide_kernel(GemmArgs a)
     // one is issued again, so the loads per chunk never change.  Groups of
     // four chunks whose loads are all main chunks take a lean path.
     static_assert(kStages == 4, "the issue distance below is kStages - 1");
-    issue(0, 0);
-    issue(min(1, nv - 1), 1);
-    issue(min(2, nv - 1), 2);
-    for (int vc0 = 0; vc0 < nv; vc0 += kStages) {
+    issue(vbeg, 0);
+    issue(min(vbeg + 1, vend - 1), 1);
+    issue(min(vbeg + 2, vend - 1), 2);
+    for (int vc0 = vbeg; vc0 < vend; vc0 += kStages) {
         if (vc0 + kStages + 2 < KC) {
 #pragma unroll
             for (int d = 0; d < kStages; ++d) {
@@ -304,8 +307,8 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_wide_kernel(GemmArgs a)
             for (int d = 0; d < kStages; ++d) {
                 const int vc = vc0 + d;
                 wait_chunk();
-                issue(min(vc + 3, nv - 1), (d + 3) % kStages);
-                if (vc < nv)
+                issue(min(vc + 3, vend - 1), (d + 3) % kStages);
+                if (vc < vend)
                     compute(d, vc < KC ? main_tiles : ext_tiles(vc));
             }
         }
@@ -325,8 +328,19 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_wide_kernel(GemmArgs a)
                     const size_t p = (size_t)(row0 + r);
                     if (kGated) {
                         const int j = slab * 4 + wave;  // gate/up pair of this wave
-                        const float v = silu_f32(acc[m][0][i]) * acc[m][1][i];
-                        a.Y[p * a.I + j * 16 + c] = (uint16_t)float_to_bf16_bits(v);
+                        const size_t h_at = p * 2 * a.I + j * 16 + c;
+                        float gate = acc[m][0][i], up = acc[m][1][i];
+                        if (a.phase == 1) {  // fp32 pre-activation for phase 2
+                            a.H[h_at] = gate;
+                            a.H[h_at + a.I] = up;
+                        } else {
+                            if (a.phase == 2) {
+                                gate += a.H[h_at];
+                                up += a.H[h_at + a.I];
+                            }
+                            a.Y[p * a.I + j * 16 + c] =
+                                (uint16_t)float_to_bf16_bits(silu_f32(gate) * up);
+                        }
                     } else {
                         const int col = slab * 128 + wave * 32 + c;
                         a.Y[p * a.n_canon + col] = (uint16_t)float_to_bf16_bits(acc[m][0][i]);

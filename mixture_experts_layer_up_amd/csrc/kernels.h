@@ -82,6 +82,12 @@ struct GemmArgs {
     int n_slabs;
     const uint16_t *zeros;    // kZeroBytes of zeros
     int lb_shared;            // LB holds one stack per adapter ([L, 1, n_canon, r])
+    // Split gate_up (the two-stream schedule): phase 1 runs the main K only
+    // and writes the fp32 pre-activation h [n, 2I] (gate columns, then up) to
+    // H; phase 2 runs the LoRA expand chunks only, adds H and applies
+    // SwiGLU.  Phase 0 does both in one pass.
+    int phase;
+    float *H;
 };
 
 // Rows per GEMM work-list tile: 16 for the decode-shaped kernel (few rows

@@ -1,6 +1,7 @@
 """Helpers for the GPU parity tests: run the HIP path, fetch results as numpy."""
 from __future__ import annotations
 
+import ctypes
 import functools
 import sys
 
@@ -32,8 +33,43 @@ def bf16_to_np(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
+_HIP = None
+
+
+def _hip():
+    global _HIP
+    if _HIP is None:
+        _HIP = ctypes.CDLL("libamdhip64.so")
+        _HIP.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        _HIP.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return _HIP
+
+
+class SideStream:
+    """A second stream (default priority) with a fork and a join event
+    (timing disabled), as the two-stream schedule takes them."""
+
+    def __init__(self):
+        self.stream = torch.cuda.Stream()
+        self.events = []
+        for _ in range(2):
+            ev = ctypes.c_void_p()
+            assert _hip().hipEventCreateWithFlags(ctypes.byref(ev), 2) == 0
+            self.events.append(ev.value)
+
+    def kwargs(self):
+        return {"side_stream": self.stream.cuda_stream, "fork_event": self.events[0],
+                "join_event": self.events[1]}
+
+    def close(self):
+        torch.cuda.synchronize()
+        for ev in self.events:
+            _hip().hipEventDestroy(ctypes.c_void_p(ev))
+        self.events = []
+
+
 def run_forward(cfg, inputs, *, use_logits=True, topk=None, mapping="given",
-                routing=False, layer=None, out=None, workspace=None):
+                routing=False, layer=None, out=None, workspace=None, side=None):
     """Forward through the C ABI; returns (out numpy float64, routing numpy dict | None)."""
     shape, lay = layer if layer is not None else binding.layer_from_host(cfg, inputs)
     kw = {}
@@ -51,6 +87,8 @@ def run_forward(cfg, inputs, *, use_logits=True, topk=None, mapping="given",
     for name in ("lora_a_gate_up", "lora_b_gate_up", "lora_a_down", "lora_b_down"):
         if name in lay:
             kw[name] = lay[name]
+    if side is not None:
+        kw.update(side.kwargs())
     o = binding.forward(shape, lay["hidden"], lay["w13_packed"], lay["w2_packed"], out=out,
                         workspace=workspace, routing=r, **kw)
     torch.cuda.synchronize()

@@ -76,7 +76,8 @@ def _inputs(**over):
     base = dict(hidden=_fake(), router_logits=_fake(), topk_ids=None, topk_weights=None,
                 w13_packed=_fake(), w2_packed=_fake(), lora_a_gate_up=_fake(),
                 lora_b_gate_up=_fake(), lora_a_down=_fake(), lora_b_down=_fake(),
-                token_lora_mapping=_fake(), stage_events=None, expert_out=None)
+                token_lora_mapping=_fake(), stage_events=None, expert_out=None,
+                side_stream=None, fork_event=None, join_event=None)
     base.update(over)
     return binding.Inputs(*[base[n] for n, _ in binding.Inputs._fields_])
 
@@ -91,6 +92,7 @@ def _inputs(**over):
     (dict(hidden=_fake(4096 + 8)), ERR_ALIGN),
     (dict(lora_a_gate_up=_fake(4096 + 2)), ERR_ALIGN),
     (dict(expert_out=_fake()), ERR_INVALID_ARG),                         # no routing export
+    (dict(side_stream=_fake()), ERR_INVALID_ARG),                        # no fork/join events
 ])
 def test_forward_argument_validation(lib, over, expect):
     shape = binding.make_shape(CONFIGS["decode64"])

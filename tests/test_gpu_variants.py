@@ -5,6 +5,10 @@
   adapter for every expert.  Checked in full, on the LoRA delta alone, on an
   expert-parallel shard (the shared stacks are not sliced by the shard), and
   through both GEMM kernels (decode tiles and the many-row tiles).
+* Two-stream schedule (the same page, Summary and Flow section 1(B)): the
+  gate_up LoRA shrink on a second stream while the main-K part of the
+  gate_up GEMM runs, joined before the expand; against the oracle, close to
+  the one-stream result, and replayed from a HIP graph.
 * External finalize (the same page, "Files changed" table, launcher row: the
   op can return the per-slot outputs with the routing instead of
   finalizing): the exported per-slot outputs against the oracle's, the
@@ -20,7 +24,7 @@ import torch
 from mixture_experts_layer_up_amd import binding
 from mixture_experts_layer_up_amd.synth import CONFIGS, make_inputs
 from oracle import oracle
-from tests._gpu import announce, bf16_to_np, run_forward, tol
+from tests._gpu import SideStream, announce, bf16_to_np, cached_inputs, run_forward, tol
 from tests.test_gpu_forward import MID, MID_EP, WIDE
 
 pytestmark = pytest.mark.gpu
@@ -127,3 +131,91 @@ def test_external_finalize_small_shapes():
                                   topk_weights=r["topk_weights"].astype(np.float64),
                                   slot_outputs=True)
         assert np.abs(y[e2p[local]] - ref_y[local]).max() <= tol(ref_y[local])
+
+
+@pytest.mark.parametrize("cfg", [MID, WIDE, SHARED_MID_EP], ids=lambda c: c.name)
+def test_two_stream_small_shapes_and_delta(cfg):
+    announce(f"forward two-stream {cfg.name}")
+    inp = make_inputs(cfg)
+    side = SideStream()
+    try:
+        layer = binding.layer_from_host(cfg, inp)
+        got, _ = run_forward(cfg, inp, layer=layer, side=side)
+        one, _ = run_forward(cfg, inp, layer=layer)
+    finally:
+        side.close()
+    ref = oracle.forward(cfg, inp)
+    assert np.abs(got - ref).max() <= tol(ref)
+    # the split GEMM sums the same products in another order: one bf16 ulp of
+    # the activation and of the output at most
+    assert np.abs(got - one).max() <= 2 ** -6 * np.abs(one).max()
+    base_cfg = cfg.replace(num_loras=0)
+    got_base, _ = run_forward(base_cfg, inp)
+    d_ref = ref - oracle.forward(base_cfg, inp)
+    bound = 1e-2 * np.abs(d_ref).max() + 2 ** -7 * np.abs(ref).max()
+    assert np.abs((got - got_base) - d_ref).max() <= bound
+
+
+@pytest.mark.parametrize("name", ["decode64", "prefill"])
+def test_two_stream_layer_configs(name):
+    announce(f"forward two-stream {name}")
+    cfg = CONFIGS[name]
+    inp = cached_inputs(name)
+    side = SideStream()
+    try:
+        got, _ = run_forward(cfg, inp, side=side)
+    finally:
+        side.close()
+    if name == "prefill":
+        rng = np.random.default_rng(56)
+        toks = np.concatenate([[0, cfg.num_tokens - 1]] +
+                              [rng.choice(np.arange(a * 512, (a + 1) * 512), 8, replace=False)
+                               for a in range(4)]).astype(np.int32)
+        ref = oracle.forward(cfg, inp, tokens=toks)
+        assert np.abs(got[toks] - ref).max() <= tol(ref)
+    else:
+        ref = oracle.forward(cfg, inp)
+        assert np.abs(got - ref).max() <= tol(ref)
+
+
+def test_two_stream_graph_replay():
+    """The two-stream forward captured into a HIP graph (the side stream joins
+    the capture through the fork event) replays bitwise equal to eager."""
+    announce("forward: two-stream HIP graph replay")
+    cfg = CONFIGS["decode64"]
+    inp = cached_inputs("decode64")
+    shape, lay = binding.layer_from_host(cfg, inp)
+    ws = torch.empty(binding.workspace_size(shape), dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    kw = {k: v for k, v in lay.items() if k not in ("hidden", "w13_packed", "w2_packed")}
+    side = SideStream()
+    try:
+        def step():
+            binding.forward(shape, lay["hidden"], lay["w13_packed"], lay["w2_packed"], out=out,
+                            workspace=ws, **kw, **side.kwargs())
+
+        step()
+        torch.cuda.synchronize()
+        eager = out.clone()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            step()
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for i in range(3):
+            out.fill_(float("nan"))
+            ws.fill_(0x33)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager), f"replay {i} differs from eager"
+            step()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager)
+        del g
+    finally:
+        side.close()

@@ -69,6 +69,11 @@ class LayerConfig:
     # shared-outer LoRA layout: A_gu [L, 1, r, H] and B_dn [L, 1, H, r] hold one
     # weight set per adapter for every expert; B_gu and A_dn stay per expert
     lora_shared_outer: bool = False
+    # routing variants: 0 = softmax renormalised over the selected experts,
+    # 1 = softmax over all experts (not renormalised); a per-expert fp32 bias
+    # N(0, routing_bias_sigma) steers the selection when sigma > 0
+    routing_method: int = 0
+    routing_bias_sigma: float = 0.0
 
     def replace(self, **kw) -> "LayerConfig":
         return dataclasses.replace(self, **kw)
@@ -139,7 +144,13 @@ def make_inputs(cfg: LayerConfig, seed: Optional[int] = None) -> Dict[str, np.nd
     else:
         hot = np.zeros(0, dtype=np.int64)
 
+    extra = {}
+    if cfg.routing_bias_sigma > 0:  # drawn last: earlier draws are unchanged
+        extra["routing_bias"] = (rng.standard_normal(E, dtype=np.float32) *
+                                 np.float32(cfg.routing_bias_sigma)).astype(np.float32)
+
     return {
+        **extra,
         "logits": np.ascontiguousarray(logits),
         "hidden": np.ascontiguousarray(hidden),
         "w13": np.ascontiguousarray(w13),

@@ -58,27 +58,36 @@ int oracle_num_threads(void)
 }
 
 /*
- * Top-k routing.  For each token: the k experts with the largest fp32
- * logits, ordered by (logit descending, expert id ascending); the weights
- * are the softmax over the k selected logits (softmax over all experts
- * followed by renormalisation over the selected ones gives the same
- * numbers).  Selection is a repeated linear scan: pick the best unpicked
- * expert k times.
+ * Top-k routing.  For each token: the k experts with the largest selection
+ * scores, ordered by (score descending, expert id ascending), where the
+ * score is the fp32 logit plus, when `bias` is given, the expert's fp32
+ * routing bias (one fp32 addition, the precision the kernel decides in).
+ * The bias only steers the choice; the weights come from the logits:
+ *   method 0: softmax over the k selected logits (softmax over all experts
+ *             followed by renormalisation over the selected ones gives the
+ *             same numbers);
+ *   method 1: softmax over all E logits, taken at the selected experts and
+ *             not renormalised.
+ * Selection is a repeated linear scan: pick the best unpicked expert k times.
  */
-int oracle_route(int T, int E, int k, const float *logits, int32_t *topk_ids,
-                 double *topk_weights)
+int oracle_route(int T, int E, int k, const float *logits, const float *bias, int method,
+                 int32_t *topk_ids, double *topk_weights)
 {
-    if (T < 0 || E <= 0 || k <= 0 || k > E)
+    if (T < 0 || E <= 0 || k <= 0 || k > E || method < 0 || method > 1)
         return -1;
     unsigned char *picked = (unsigned char *)malloc((size_t)E);
     double *ex = (double *)malloc((size_t)k * sizeof(double));
-    if (!picked || !ex) {
+    float *score = (float *)malloc((size_t)E * sizeof(float));
+    if (!picked || !ex || !score) {
         free(picked);
         free(ex);
+        free(score);
         return -2;
     }
     for (int t = 0; t < T; ++t) {
         const float *row = logits + (size_t)t * E;
+        for (int e = 0; e < E; ++e)
+            score[e] = bias ? row[e] + bias[e] : row[e];
         memset(picked, 0, (size_t)E);
         for (int j = 0; j < k; ++j) {
             int best = -1;
@@ -86,23 +95,32 @@ int oracle_route(int T, int E, int k, const float *logits, int32_t *topk_ids,
                 if (picked[e])
                     continue;
                 /* strict '>' keeps the lower id on an exact tie */
-                if (best < 0 || row[e] > row[best])
+                if (best < 0 || score[e] > score[best])
                     best = e;
             }
             picked[best] = 1;
             topk_ids[(size_t)t * k + j] = best;
         }
-        double m = (double)row[topk_ids[(size_t)t * k]];
+        /* the largest logit the softmax runs over, for a safe shift */
+        double m = -INFINITY;
+        for (int e = 0; e < E; ++e)
+            if ((method == 1 || picked[e]) && (double)row[e] > m)
+                m = (double)row[e];
         double sum = 0.0;
         for (int j = 0; j < k; ++j) {
             ex[j] = exp((double)row[topk_ids[(size_t)t * k + j]] - m);
-            sum += ex[j];
+            if (method == 0)
+                sum += ex[j];
         }
+        if (method == 1)
+            for (int e = 0; e < E; ++e)
+                sum += exp((double)row[e] - m);
         for (int j = 0; j < k; ++j)
             topk_weights[(size_t)t * k + j] = ex[j] / sum;
     }
     free(picked);
     free(ex);
+    free(score);
     return 0;
 }
 

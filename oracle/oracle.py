@@ -40,7 +40,7 @@ def _load():
         i32, f64 = ctypes.c_int, ctypes.c_double
         vp = ctypes.c_void_p
         lib.oracle_num_threads.restype = i32
-        lib.oracle_route.argtypes = [i32, i32, i32, vp, vp, vp]
+        lib.oracle_route.argtypes = [i32, i32, i32, vp, vp, i32, vp, vp]
         lib.oracle_route.restype = i32
         lib.oracle_permute.argtypes = [i32] * 6 + [vp] * 8
         lib.oracle_permute.restype = i32
@@ -58,13 +58,19 @@ def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
 
-def route(logits: np.ndarray, top_k: int):
-    """Top-k ids [T,k] int32 and fp64 softmax weights [T,k] of fp32 logits [T,E]."""
+def route(logits: np.ndarray, top_k: int, bias: Optional[np.ndarray] = None, method: int = 0):
+    """Top-k ids [T,k] int32 and fp64 weights [T,k] of fp32 logits [T,E].
+
+    ``bias`` (fp32 [E]) is added to the logits for the selection only;
+    ``method`` 0 renormalises the softmax over the selected experts, 1 takes
+    the softmax over all experts at the selected ones."""
     logits = np.ascontiguousarray(logits, dtype=np.float32)
     T, E = logits.shape
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    assert b is None or b.shape == (E,)
     ids = np.empty((T, top_k), dtype=np.int32)
     w = np.empty((T, top_k), dtype=np.float64)
-    rc = _load().oracle_route(T, E, top_k, _ptr(logits), _ptr(ids), _ptr(w))
+    rc = _load().oracle_route(T, E, top_k, _ptr(logits), _ptr(b), int(method), _ptr(ids), _ptr(w))
     if rc != 0:
         raise RuntimeError(f"oracle_route failed ({rc})")
     return ids, w
@@ -114,8 +120,8 @@ def forward(cfg, inputs: Dict[str, np.ndarray], topk_ids: Optional[np.ndarray] =
     T, H, I = cfg.num_tokens, cfg.hidden, cfg.inter
     k = cfg.top_k
     if topk_ids is None:
-        logits = inputs["logits"]
-        ids, w = route(logits, k)
+        ids, w = route(inputs["logits"], k, bias=inputs.get("routing_bias"),
+                       method=getattr(cfg, "routing_method", 0))
         topk_ids, topk_weights = ids, w
     ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
     w = np.ascontiguousarray(topk_weights, dtype=np.float64)

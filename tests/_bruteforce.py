@@ -21,15 +21,25 @@ def f64(bits: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(bits).astype(np.float64)
 
 
-def route(logits: np.ndarray, k: int):
+def route(logits: np.ndarray, k: int, bias=None, method: int = 0):
+    """Selection by (logit + bias in fp32, desc; id asc); weights from the
+    logits: softmax over the selected (method 0) or over all experts taken at
+    the selected ones (method 1)."""
     T, E = logits.shape
     ids = np.empty((T, k), dtype=np.int32)
     w = np.empty((T, k), dtype=np.float64)
     for t in range(T):
         row = [float(v) for v in logits[t]]
-        order = sorted(range(E), key=lambda e: (-row[e], e))[:k]
+        if bias is None:
+            score = row
+        else:
+            score = [float(np.float32(logits[t, e]) + np.float32(bias[e])) for e in range(E)]
+        order = sorted(range(E), key=lambda e: (-score[e], e))[:k]
         ids[t] = order
-        w[t] = softmax(np.array([row[e] for e in order], dtype=np.float64))
+        if method == 0:
+            w[t] = softmax(np.array([row[e] for e in order], dtype=np.float64))
+        else:
+            w[t] = softmax(np.array(row, dtype=np.float64))[order]
     return ids, w
 
 
@@ -90,7 +100,8 @@ def slot_outputs(cfg, inp, topk_ids):
 def forward(cfg, inp, topk_ids=None, topk_weights=None):
     T, H, k = cfg.num_tokens, cfg.hidden, cfg.top_k
     if topk_ids is None:
-        topk_ids, topk_weights = route(inp["logits"], k)
+        topk_ids, topk_weights = route(inp["logits"], k, bias=inp.get("routing_bias"),
+                                       method=getattr(cfg, "routing_method", 0))
     out = np.zeros((T, H), dtype=np.float64)
     for (t, j), v in sorted(_slot_ffns(cfg, inp, topk_ids).items()):
         if v is not None:

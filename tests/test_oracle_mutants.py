@@ -38,7 +38,12 @@ MUTANTS = [
      "h[n] += v;", "h[n] += v * topk_weights[(size_t)t * k + j];", 0),
     ("down_lora_unweighted", "y[n] += v;",
      "y[n] += v / topk_weights[(size_t)t * k + j];", 0),
-    ("tie_prefers_high_id", "row[e] > row[best]", "row[e] >= row[best]", 0),
+    ("tie_prefers_high_id", "score[e] > score[best]", "score[e] >= score[best]", 0),
+    ("bias_ignored", "score[e] = bias ? row[e] + bias[e] : row[e];", "score[e] = row[e];", 0),
+    ("bias_enters_weights", "ex[j] = exp((double)row[topk_ids[(size_t)t * k + j]] - m);",
+     "ex[j] = exp((double)score[topk_ids[(size_t)t * k + j]] - m);", 0),
+    ("method1_renormalised", "if (method == 0)\n                sum += ex[j];",
+     "sum += ex[j];", 0),
     ("weights_not_normalised", "topk_weights[(size_t)t * k + j] = ex[j] / sum;",
      "topk_weights[(size_t)t * k + j] = ex[j];", 0),
     ("ep_window_off_by_one", "if (!(id >= off && id < off + E_l))",
@@ -104,6 +109,14 @@ def _battery_passes() -> bool:
                                               "lora_seg_offsets", "lora_seg_slots")], ref_p):
                 if not np.array_equal(a, b):
                     return False
+        for E, k, method in ((16, 4, 0), (16, 4, 1), (40, 5, 1)):
+            rng = np.random.default_rng(300 + E + method)
+            lg = rng.standard_normal((9, E), dtype=np.float32)
+            bias = rng.standard_normal(E, dtype=np.float32)
+            ids, w = oracle.route(lg, k, bias=bias, method=method)
+            ids_r, w_r = bf.route(lg, k, bias=bias, method=method)
+            if not (np.array_equal(ids, ids_r) and np.allclose(w, w_r, rtol=1e-13, atol=0)):
+                return False
         for cfg in (MINI_SHARED, MINI_EP_SHARED):
             inp = make_inputs(cfg)
             out = oracle.forward(cfg, inp)

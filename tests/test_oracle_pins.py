@@ -382,3 +382,51 @@ def test_slot_outputs_match_bruteforce(cfg):
     T, k, H = cfg.num_tokens, cfg.top_k, cfg.hidden
     summed = (w.reshape(T, k, 1) * y.reshape(T, k, H)).sum(axis=1) * cfg.routed_scaling_factor
     assert np.abs(out - summed).max() <= _tol(out)
+
+
+# --------------------------------------------------------------------------
+# routing variants: a selection bias and the softmax over all experts (the
+# pages name a routing bias and a routing method without defining them; the
+# readings are a bias added to the logits for the choice only, and method 1 =
+# softmax over all experts taken at the chosen ones, not renormalised)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("E,k,method", [(8, 2, 0), (8, 2, 1), (33, 4, 0), (33, 4, 1),
+                                        (128, 8, 1), (5, 5, 1)])
+def test_route_with_bias_matches_sorted_bruteforce(E, k, method):
+    rng = np.random.default_rng(400 + E + 7 * method)
+    logits = rng.standard_normal((11, E), dtype=np.float32)
+    bias = rng.standard_normal(E, dtype=np.float32)
+    ids, w = oracle.route(logits, k, bias=bias, method=method)
+    ids_r, w_r = bf.route(logits, k, bias=bias, method=method)
+    np.testing.assert_array_equal(ids, ids_r)
+    np.testing.assert_allclose(w, w_r, rtol=1e-13, atol=0)
+
+
+def test_route_variant_special_cases():
+    rng = np.random.default_rng(420)
+    logits = rng.standard_normal((9, 16), dtype=np.float32)
+    ids0, w0 = oracle.route(logits, 4)
+    # a zero bias changes nothing
+    ids, w = oracle.route(logits, 4, bias=np.zeros(16, np.float32))
+    np.testing.assert_array_equal(ids, ids0)
+    np.testing.assert_array_equal(w, w0)
+    # a huge bias on one expert puts it first for every token; its weight still
+    # comes from its (unbiased) logit
+    bias = np.zeros(16, np.float32)
+    bias[11] = 1000.0
+    ids, w = oracle.route(logits, 4, bias=bias)
+    assert np.all(ids[:, 0] == 11)
+    for t in range(9):
+        sel = logits[t, ids[t]].astype(np.float64)
+        np.testing.assert_allclose(w[t], softmax(sel), rtol=1e-13)
+    # method 1: the selected entries of the full softmax; they sum to 1 only
+    # when every expert is selected
+    ids1, w1 = oracle.route(logits, 4, method=1)
+    np.testing.assert_array_equal(ids1, ids0)
+    full = softmax(logits.astype(np.float64), axis=1)
+    np.testing.assert_allclose(w1, np.take_along_axis(full, ids1.astype(np.int64), axis=1),
+                               rtol=1e-13)
+    assert np.all(w1.sum(axis=1) < 1.0)
+    _, w_all = oracle.route(logits, 16, method=1)
+    np.testing.assert_allclose(w_all.sum(axis=1), 1.0, rtol=1e-13)

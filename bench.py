@@ -233,7 +233,8 @@ def cpu_baseline(cfg, inp, min_seconds: float):
     T = cfg.num_tokens
     n_tok = min(T, 64)
     toks = np.linspace(0, T - 1, n_tok).astype(np.int32) if n_tok < T else None
-    ids, w = oracle.route(inp["logits"], cfg.top_k)
+    ids, w = oracle.route(inp["logits"], cfg.top_k, bias=inp.get("routing_bias"),
+                          method=getattr(cfg, "routing_method", 0))
     t0 = time.perf_counter()
     reps = 0
     while True:
@@ -259,6 +260,10 @@ def main():
     ap.add_argument("--finalize", default="fused", choices=("fused", "external"),
                     help="external: the forward exports per-slot outputs and a separate "
                          "finalize call completes the step")
+    ap.add_argument("--routing-method", type=int, default=0, choices=(0, 1),
+                    help="0: softmax over the selected experts; 1: over all experts")
+    ap.add_argument("--routing-bias-sigma", type=float, default=0.0,
+                    help="> 0: a per-expert selection bias drawn N(0, sigma)")
     ap.add_argument("--two-stream", type=int, default=0,
                     help="1: gate_up LoRA shrink on a second stream, concurrent with the "
                          "main-K part of the gate_up GEMM")
@@ -299,6 +304,9 @@ def main():
     cfg = CONFIGS[args.workload]
     if args.lora_layout == "shared_outer":
         cfg = cfg.replace(lora_shared_outer=True)
+    if args.routing_method or args.routing_bias_sigma > 0:
+        cfg = cfg.replace(routing_method=args.routing_method,
+                          routing_bias_sigma=args.routing_bias_sigma)
     log(f"[bench] generating {args.workload} inputs")
     inp = make_inputs(cfg)
     torch.cuda.set_device(0)
@@ -452,6 +460,8 @@ def main():
                    "local_num_experts": cfg.local_num_experts, "num_loras": cfg.num_loras,
                    "rank": cfg.rank_gate_up, "lora_layout": args.lora_layout,
                    "finalize": args.finalize, "two_stream": bool(args.two_stream),
+                   "routing_method": args.routing_method,
+                   "routing_bias_sigma": args.routing_bias_sigma,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "gemm_gate_up_swiglu",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

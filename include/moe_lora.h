@@ -68,7 +68,8 @@ extern "C" {
  *   local_expert_offset + local_num_experts <= num_experts
  *   0 <= num_loras <= 64, num_loras * local_num_experts <= 8192
  *   0 <= rank_gate_up, rank_down <= 256
- *   lora_shared_outer is 0 or 1 (else MOE_LORA_ERR_INVALID_ARG)
+ *   lora_shared_outer is 0 or 1, routing_method is 0 or 1 (else
+ *   MOE_LORA_ERR_INVALID_ARG)
  * A LoRA projection is active when num_loras > 0 and its rank > 0.
  *
  * lora_shared_outer = 1 selects the shared-outer LoRA layout ("BF16 support
@@ -91,13 +92,18 @@ typedef struct moe_lora_shape {
     int32_t rank_down;             /* r_dn */
     float routed_scaling_factor;   /* multiplies the routed sum (1.0 = none) */
     int32_t lora_shared_outer;     /* 0: per-expert LoRA stacks; 1: shared-outer */
+    int32_t routing_method;        /* weights from router logits: 0 = softmax over
+                                      the k selected logits; 1 = softmax over all
+                                      E logits at the selected experts, not
+                                      renormalised */
 } moe_lora_shape;
 
 /*
  * Routing results (device arrays, caller-owned).  Slot x = t * top_k + j.
  *   topk_ids      [T, k] int32  global expert ids, ordered by (logit desc,
  *                               id asc)
- *   topk_weights  [T, k] fp32   softmax over the k selected logits
+ *   topk_weights  [T, k] fp32   per routing_method (method 0: softmax over
+ *                               the k selected logits)
  *   expert_counts [E_l]         local slots per local expert
  *   expert_offsets[E_l + 1]     exclusive prefix sum; [E_l] = P, the number
  *                               of local slots
@@ -127,6 +133,13 @@ typedef struct moe_lora_routing {
  * (`topk_ids`, `topk_weights`) is given.
  *   hidden             bf16 [T, H], 16-byte aligned
  *   router_logits      fp32 [T, E]
+ *   routing_bias       fp32 [E] or NULL: added to the logits (one fp32 add)
+ *                      for the choice of experts only; the weights still
+ *                      come from the logits.  The pages name a routing bias
+ *                      without defining it ("BF16 support for the
+ *                      experimental_sgl_trtllm MoE-LoRA path", "Files
+ *                      changed" table, launcher row); this is the reading
+ *                      taken.  Ignored when top-k is given.
  *   topk_ids           int32 [T, k] (any value; out-of-window ids are
  *                      non-local slots), topk_weights fp32 [T, k]
  *   w13_packed         expert gate_up weights [E_l, H, 2I] (columns [0, I)
@@ -180,6 +193,7 @@ typedef struct moe_lora_routing {
 typedef struct moe_lora_inputs {
     const void *hidden;
     const float *router_logits;
+    const float *routing_bias;
     const int32_t *topk_ids;
     const float *topk_weights;
     const void *w13_packed;
@@ -225,14 +239,15 @@ int moe_lora_pack_weights(const moe_lora_shape *shape, const void *w13, const vo
                           void *w13_packed, void *w2_packed, void *stream);
 
 /*
- * Routing and permutation only.  Routes from `router_logits` when given,
- * else takes `topk_ids` / `topk_weights` as they are (then routing->topk_ids
+ * Routing and permutation only.  Routes from `router_logits` (with the
+ * optional `routing_bias`, as in moe_lora_inputs) when given, else takes
+ * `topk_ids` / `topk_weights` as they are (then routing->topk_ids
  * and routing->topk_weights are not written and may be NULL).  Every other
  * field of `routing` must be non-NULL.  `token_lora_mapping` as in
  * moe_lora_inputs.  Needs no workspace.
  */
 int moe_lora_route(const moe_lora_shape *shape, const float *router_logits,
-                   const int32_t *topk_ids, const float *topk_weights,
+                   const float *routing_bias, const int32_t *topk_ids, const float *topk_weights,
                    const int32_t *token_lora_mapping, const moe_lora_routing *routing,
                    void *stream);
 

@@ -36,6 +36,7 @@ class Shape(ctypes.Structure):
         ("rank_down", ctypes.c_int32),
         ("routed_scaling_factor", ctypes.c_float),
         ("lora_shared_outer", ctypes.c_int32),
+        ("routing_method", ctypes.c_int32),
     ]
 
 
@@ -48,7 +49,8 @@ class Routing(ctypes.Structure):
 
 class Inputs(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in (
-        "hidden", "router_logits", "topk_ids", "topk_weights", "w13_packed", "w2_packed",
+        "hidden", "router_logits", "routing_bias", "topk_ids", "topk_weights", "w13_packed",
+        "w2_packed",
         "lora_a_gate_up", "lora_b_gate_up", "lora_a_down", "lora_b_down",
         "token_lora_mapping", "stage_events", "expert_out", "side_stream", "fork_event",
         "join_event")]
@@ -83,7 +85,7 @@ def load_library(path: str = LIB_PATH):
     lib.moe_lora_packed_w2_bytes.restype = ctypes.c_size_t
     lib.moe_lora_pack_weights.argtypes = [P(Shape), vp, vp, vp, vp, vp]
     lib.moe_lora_pack_weights.restype = ctypes.c_int
-    lib.moe_lora_route.argtypes = [P(Shape), vp, vp, vp, vp, P(Routing), vp]
+    lib.moe_lora_route.argtypes = [P(Shape), vp, vp, vp, vp, vp, P(Routing), vp]
     lib.moe_lora_route.restype = ctypes.c_int
     lib.moe_lora_forward.argtypes = [P(Shape), P(Inputs), P(Routing), vp, vp, ctypes.c_size_t, vp]
     lib.moe_lora_forward.restype = ctypes.c_int
@@ -106,7 +108,8 @@ def make_shape(cfg) -> Shape:
     return Shape(cfg.num_tokens, cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k,
                  cfg.local_expert_offset, cfg.local_num_experts, cfg.num_loras,
                  cfg.rank_gate_up, cfg.rank_down, float(cfg.routed_scaling_factor),
-                 int(bool(getattr(cfg, "lora_shared_outer", False))))
+                 int(bool(getattr(cfg, "lora_shared_outer", False))),
+                 int(getattr(cfg, "routing_method", 0)))
 
 
 def _check(rc: int):
@@ -175,7 +178,8 @@ def _routing_struct(r: Dict[str, torch.Tensor]) -> Routing:
 def route(shape: Shape, router_logits: Optional[torch.Tensor] = None,
           topk_ids: Optional[torch.Tensor] = None, topk_weights: Optional[torch.Tensor] = None,
           token_lora_mapping: Optional[torch.Tensor] = None,
-          routing: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+          routing: Optional[Dict[str, torch.Tensor]] = None,
+          routing_bias: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     T, E, k = shape.num_tokens, shape.num_experts, shape.top_k
     dev = (router_logits if router_logits is not None else topk_ids).device
     r = routing if routing is not None else alloc_routing(shape, dev)
@@ -183,6 +187,7 @@ def route(shape: Shape, router_logits: Optional[torch.Tensor] = None,
     _check(load_library().moe_lora_route(
         ctypes.byref(shape),
         _ptr(router_logits, torch.float32, (T, E), "router_logits"),
+        _ptr(routing_bias, torch.float32, (E,), "routing_bias"),
         _ptr(topk_ids, torch.int32, (T, k), "topk_ids"),
         _ptr(topk_weights, torch.float32, (T, k), "topk_weights"),
         _ptr(token_lora_mapping, torch.int32, (T,), "token_lora_mapping"),
@@ -193,7 +198,7 @@ def route(shape: Shape, router_logits: Optional[torch.Tensor] = None,
 def forward(shape: Shape, hidden: torch.Tensor, w13_packed: torch.Tensor,
             w2_packed: torch.Tensor, lora_a_gate_up=None, lora_b_gate_up=None,
             lora_a_down=None, lora_b_down=None, token_lora_mapping=None,
-            router_logits=None, topk_ids=None, topk_weights=None,
+            router_logits=None, topk_ids=None, topk_weights=None, routing_bias=None,
             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
             routing: Optional[Dict[str, torch.Tensor]] = None,
             stage_events: Optional[Sequence[int]] = None,
@@ -226,6 +231,7 @@ def forward(shape: Shape, hidden: torch.Tensor, w13_packed: torch.Tensor,
     inputs = Inputs(
         _ptr(hidden, _BF16, (T, H), "hidden"),
         _ptr(router_logits, torch.float32, (T, E), "router_logits"),
+        _ptr(routing_bias, torch.float32, (E,), "routing_bias"),
         _ptr(topk_ids, torch.int32, (T, k), "topk_ids"),
         _ptr(topk_weights, torch.float32, (T, k), "topk_weights"),
         _ptr(w13_packed, _BF16, (E_l, H, 2 * I), "w13_packed"),
@@ -289,6 +295,8 @@ def layer_from_host(cfg, inputs: Dict, device="cuda"):
         "w2_packed": w2p,
         "token_lora_mapping": torch.from_numpy(inputs["mapping"]).to(device),
     }
+    if inputs.get("routing_bias") is not None:
+        layer["routing_bias"] = torch.from_numpy(inputs["routing_bias"]).to(device)
     if L > 0 and cfg.rank_gate_up > 0:
         layer["lora_a_gate_up"] = dev_bf16(inputs["a_gu"])
         layer["lora_b_gate_up"] = dev_bf16(inputs["b_gu"])

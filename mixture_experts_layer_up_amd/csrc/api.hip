@@ -56,6 +56,8 @@ int validate_shape(const moe_lora_shape *s)
         return MOE_LORA_ERR_INVALID_ARG;
     if (s->lora_shared_outer != 0 && s->lora_shared_outer != 1)
         return MOE_LORA_ERR_INVALID_ARG;
+    if (s->routing_method != 0 && s->routing_method != 1)
+        return MOE_LORA_ERR_INVALID_ARG;
     return MOE_LORA_OK;
 }
 
@@ -121,13 +123,15 @@ struct RoutingPtrs {
     int32_t *counts, *offsets, *exp2perm, *perm2exp, *seg_offsets, *seg_slots;
 };
 
-int enqueue_routing(const moe_lora_shape *s, const float *logits, const int32_t *topk_ids,
-                    const int32_t *mapping, const RoutingPtrs &r, hipStream_t st,
+int enqueue_routing(const moe_lora_shape *s, const float *logits, const float *bias,
+                    const int32_t *topk_ids, const int32_t *mapping, const RoutingPtrs &r,
+                    hipStream_t st,
                     int4 *tiles = nullptr, int tile_rows = 0, int max_tiles = 0,
                     int32_t *tile_count = nullptr, void *zeros = nullptr)
 {
     if (logits) {
-        RouteArgs ra{logits, r.ids, r.weights, s->num_tokens, s->num_experts, s->top_k};
+        RouteArgs ra{logits, r.ids, r.weights, s->num_tokens, s->num_experts, s->top_k,
+                     bias, s->routing_method};
         MOE_TRY(check(launch_route(ra, st)));
     }
     PermuteArgs pa{};
@@ -222,7 +226,7 @@ int moe_lora_pack_weights(const moe_lora_shape *shape, const void *w13, const vo
 }
 
 int moe_lora_route(const moe_lora_shape *shape, const float *router_logits,
-                   const int32_t *topk_ids, const float *topk_weights,
+                   const float *routing_bias, const int32_t *topk_ids, const float *topk_weights,
                    const int32_t *token_lora_mapping, const moe_lora_routing *routing,
                    void *stream)
 {
@@ -246,7 +250,7 @@ int moe_lora_route(const moe_lora_shape *shape, const float *router_logits,
                   routing->expert_offsets, routing->expanded_idx_to_permuted_idx,
                   routing->permuted_idx_to_expanded_idx, routing->lora_seg_offsets,
                   routing->lora_seg_slots};
-    return enqueue_routing(shape, router_logits, topk_ids, token_lora_mapping, r,
+    return enqueue_routing(shape, router_logits, routing_bias, topk_ids, token_lora_mapping, r,
                            static_cast<hipStream_t>(stream));
 }
 
@@ -342,7 +346,8 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     int4 *tiles = reinterpret_cast<int4 *>(ws + lay.tiles);
     void *zeros = ws + lay.zeros;
     int32_t *tile_count = reinterpret_cast<int32_t *>(ws + lay.tile_count);
-    MOE_TRY(enqueue_routing(shape, in->router_logits, in->topk_ids, in->token_lora_mapping, r, st,
+    MOE_TRY(enqueue_routing(shape, in->router_logits, in->routing_bias, in->topk_ids,
+                            in->token_lora_mapping, r, st,
                             tiles, lay.tile_rows, lay.max_tiles, tile_count, zeros));
     MOE_TRY(record(ev, 1, st));
 

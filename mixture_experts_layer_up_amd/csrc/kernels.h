@@ -12,6 +12,8 @@ struct RouteArgs {
     int32_t *topk_ids;     // [T, k]
     float *topk_weights;   // [T, k]
     int T, E, k;
+    const float *bias;     // [E] selection bias, or null
+    int method;            // 0: softmax over the selected; 1: softmax over all E
 };
 
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;

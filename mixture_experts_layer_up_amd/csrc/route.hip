@@ -3,9 +3,13 @@
 // The pages' launcher starts its pipeline with a routing stage that turns
 // router output into top-k expert ids and weights ("BF16 support for the
 // experimental_sgl_trtllm MoE-LoRA path", "Files changed" table, launcher
-// row).  Reading taken here: the k largest fp32 logits, ordered by (logit
-// descending, expert id ascending); weights are the softmax over the k
-// selected logits (renormalised top-k softmax).
+// row; the op also names a routing bias and a routing method, undefined).
+// Readings taken here: the k largest selection scores, ordered by (score
+// descending, expert id ascending), where the score is the fp32 logit plus
+// the expert's fp32 bias when one is given; weights come from the logits:
+// the softmax over the k selected logits (method 0, renormalised top-k
+// softmax) or the softmax over all E logits at the selected experts
+// (method 1).
 //
 // Selection as a wave-level radix select.  Each (logit, id) becomes one
 // 42-bit key that orders exactly like (logit descending, id ascending): the
@@ -48,15 +52,18 @@ __global__ __launch_bounds__(256) void route_topk_kernel(RouteArgs a)
     unsigned long long thr = 0;
     if (active) {
         const float *row = a.logits + (size_t)t * a.E;
+        float bv[NV];
 #pragma unroll
         for (int i = 0; i < NV; ++i) {  // all loads first, then the keys
             const int e = lane + kWave * i;
             val[i] = e < a.E ? row[e] : 0.0f;
+            bv[i] = (a.bias && e < a.E) ? a.bias[e] : 0.0f;
         }
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int e = lane + kWave * i;
-            key[i] = e < a.E ? route_key(val[i], e) : 0ull;  // 0 ranks below every real key
+            const float score = a.bias ? val[i] + bv[i] : val[i];  // one fp32 add
+            key[i] = e < a.E ? route_key(score, e) : 0ull;  // 0 ranks below every real key
         }
         // the k-th largest key: the largest threshold with >= k keys at or above it
         for (int b = 41; b >= 0; --b) {
@@ -95,9 +102,26 @@ __global__ __launch_bounds__(256) void route_topk_kernel(RouteArgs a)
     __syncthreads();
     if (!active)
         return;
-    const float m = sel_val[wave][0];
+    // the softmax's shift: the largest logit it runs over (selected, or all)
+    float m = lane < k ? sel_val[wave][lane] : -INFINITY;
+    if (a.method == 1) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (lane + kWave * i < a.E)
+                m = fmaxf(m, val[i]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        m = fmaxf(m, __shfl_xor(m, off));
     const float ex = lane < k ? expf(sel_val[wave][lane] - m) : 0.0f;
     float sum = ex;
+    if (a.method == 1) {  // the denominator runs over every expert
+        sum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (lane + kWave * i < a.E)
+                sum += expf(val[i] - m);
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1)
         sum += __shfl_xor(sum, off);  // xor butterfly: identical sum on every lane

@@ -75,6 +75,8 @@ def run_forward(cfg, inputs, *, use_logits=True, topk=None, mapping="given",
     kw = {}
     if use_logits:
         kw["router_logits"] = lay["router_logits"]
+        if "routing_bias" in lay:
+            kw["routing_bias"] = lay["routing_bias"]
     else:
         ids, w = topk
         kw["topk_ids"] = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()

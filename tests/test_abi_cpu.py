@@ -65,7 +65,7 @@ def test_invalid_shapes_rejected(lib, field, value):
     shape = binding.make_shape(cfg)
     rs = binding.Routing()
     assert lib.moe_lora_route(ctypes.byref(shape), ctypes.c_void_p(256), None, None, None,
-                              ctypes.byref(rs), None) == ERR_SHAPE
+                              None, ctypes.byref(rs), None) == ERR_SHAPE
 
 
 def _fake(addr=4096):
@@ -73,7 +73,8 @@ def _fake(addr=4096):
 
 
 def _inputs(**over):
-    base = dict(hidden=_fake(), router_logits=_fake(), topk_ids=None, topk_weights=None,
+    base = dict(hidden=_fake(), router_logits=_fake(), routing_bias=None, topk_ids=None,
+                topk_weights=None,
                 w13_packed=_fake(), w2_packed=_fake(), lora_a_gate_up=_fake(),
                 lora_b_gate_up=_fake(), lora_a_down=_fake(), lora_b_down=_fake(),
                 token_lora_mapping=_fake(), stage_events=None, expert_out=None,
@@ -129,9 +130,9 @@ def test_lora_pointers_optional_when_inactive(lib):
 def test_route_and_pack_validation(lib):
     shape = binding.make_shape(CONFIGS["tiny"])
     rs = binding.Routing()   # all NULL
-    assert lib.moe_lora_route(ctypes.byref(shape), _fake(), None, None, None,
+    assert lib.moe_lora_route(ctypes.byref(shape), _fake(), None, None, None, None,
                               ctypes.byref(rs), None) == ERR_INVALID_ARG
-    assert lib.moe_lora_route(ctypes.byref(shape), None, None, None, None,
+    assert lib.moe_lora_route(ctypes.byref(shape), None, None, None, None, None,
                               None, None) == ERR_INVALID_ARG
     assert lib.moe_lora_pack_weights(ctypes.byref(shape), None, _fake(), _fake(), _fake(),
                                      None) == ERR_INVALID_ARG
@@ -187,3 +188,13 @@ def test_shared_outer_flag_validation(lib):
     inp = _inputs()
     assert lib.moe_lora_forward(ctypes.byref(shape), ctypes.byref(inp), None, _fake(),
                                 _fake(1 << 20), 1 << 30, None) == ERR_INVALID_ARG
+
+
+def test_routing_method_validation(lib):
+    shape = binding.make_shape(CONFIGS["decode64"].replace(routing_method=1))
+    assert shape.routing_method == 1 and binding.workspace_size(shape) > 0
+    shape.routing_method = 2
+    assert binding.workspace_size(shape) == 0
+    rs = _routing_fake()
+    assert lib.moe_lora_route(ctypes.byref(shape), _fake(), None, None, None, None,
+                              ctypes.byref(rs), None) == ERR_INVALID_ARG

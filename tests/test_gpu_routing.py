@@ -19,9 +19,11 @@ INT_FIELDS = ["expert_counts", "expert_offsets", "expanded_idx_to_permuted_idx",
               "permuted_idx_to_expanded_idx", "lora_seg_offsets", "lora_seg_slots"]
 
 
-def _gpu_route(cfg, logits=None, topk=None, mapping=None):
+def _gpu_route(cfg, logits=None, topk=None, mapping=None, bias=None):
     shape = binding.make_shape(cfg)
     kw = {}
+    if bias is not None:
+        kw["routing_bias"] = torch.from_numpy(np.ascontiguousarray(bias, np.float32)).cuda()
     if logits is not None:
         kw["router_logits"] = torch.from_numpy(np.ascontiguousarray(logits, np.float32)).cuda()
     else:
@@ -34,9 +36,9 @@ def _gpu_route(cfg, logits=None, topk=None, mapping=None):
     return {k: v.cpu().numpy() for k, v in r.items()}
 
 
-def _check_against_oracle(cfg, logits, mapping):
-    got = _gpu_route(cfg, logits=logits, mapping=mapping)
-    ids, w = oracle.route(logits, cfg.top_k)
+def _check_against_oracle(cfg, logits, mapping, bias=None):
+    got = _gpu_route(cfg, logits=logits, mapping=mapping, bias=bias)
+    ids, w = oracle.route(logits, cfg.top_k, bias=bias, method=cfg.routing_method)
     np.testing.assert_array_equal(got["topk_ids"], ids)
     np.testing.assert_allclose(got["topk_weights"], w, rtol=1e-6, atol=1e-7)
     ref = oracle.permute(ids, mapping, cfg.num_experts, cfg.local_expert_offset,
@@ -92,3 +94,22 @@ def test_topk_passthrough_with_invalid_ids():
     ref = oracle.permute(ids, mapping, 128, 32, 32, 4)
     for name in INT_FIELDS:
         np.testing.assert_array_equal(got[name], ref[name], err_msg=name)
+
+
+
+@pytest.mark.parametrize("E,k,method,with_bias", [
+    (128, 8, 0, True), (128, 8, 1, False), (128, 8, 1, True), (100, 7, 1, True),
+    (1024, 64, 1, True), (16, 16, 1, False), (33, 3, 0, True)])
+def test_routing_variants(E, k, method, with_bias):
+    """Selection bias (choice only) and softmax over all experts: ids bit-exact,
+    weights to 1e-6 (the readings of the pages' undefined routing bias and
+    routing method that the oracle takes)."""
+    announce(f"routing variant E={E} k={k} method={method} bias={with_bias}")
+    T = 77
+    cfg = CONFIGS["tiny"].replace(num_tokens=T, num_experts=E, top_k=k, local_num_experts=E,
+                                  num_loras=2, routing_method=method)
+    rng = np.random.default_rng(E + k + 10 * method)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    bias = rng.standard_normal(E).astype(np.float32) if with_bias else None
+    mapping = rng.integers(-1, 2, size=T).astype(np.int32)
+    _check_against_oracle(cfg, logits, mapping, bias=bias)

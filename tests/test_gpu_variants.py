@@ -9,6 +9,9 @@
   gate_up LoRA shrink on a second stream while the main-K part of the
   gate_up GEMM runs, joined before the expand; against the oracle, close to
   the one-stream result, and replayed from a HIP graph.
+* Routing variants (the same page names a routing bias and a routing method
+  without defining them): a selection-only bias and the softmax over all
+  experts, through the whole layer.
 * External finalize (the same page, "Files changed" table, launcher row: the
   op can return the per-slot outputs with the routing instead of
   finalizing): the exported per-slot outputs against the oracle's, the
@@ -219,3 +222,16 @@ def test_two_stream_graph_replay():
         del g
     finally:
         side.close()
+
+
+@pytest.mark.parametrize("method,bias_sigma", [(0, 1.0), (1, 0.0), (1, 1.0)])
+def test_routing_variants_through_the_layer(method, bias_sigma):
+    cfg = CONFIGS["decode64"].replace(name=f"route_m{method}_b{bias_sigma}",
+                                      routing_method=method, routing_bias_sigma=bias_sigma)
+    announce(f"forward {cfg.name}")
+    inp = make_inputs(cfg)
+    got, r = run_forward(cfg, inp, routing=True)
+    ids, w = oracle.route(inp["logits"], cfg.top_k, bias=inp.get("routing_bias"), method=method)
+    np.testing.assert_array_equal(r["topk_ids"], ids)
+    ref = oracle.forward(cfg, inp)
+    assert np.abs(got - ref).max() <= tol(ref)

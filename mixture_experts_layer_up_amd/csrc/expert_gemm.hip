@@ -461,7 +461,7 @@ __global__ __launch_bounds__(256, 2) void lora_shrink_kernel(ShrinkArgs a)
 template <int MT, int CH, bool kGated>
 hipError_t launch_gemm_variant(const GemmArgs &a, hipStream_t s)
 {
-    const int blocks = a.n_tiles * a.n_slabs;
+    const int blocks = gemm_grid_blocks(a.n_tiles, a.n_slabs);
     if (blocks <= 0)
         return hipSuccess;
     if ((a.r & 7) == 0)

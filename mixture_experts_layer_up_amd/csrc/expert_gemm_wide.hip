@@ -361,7 +361,7 @@ bool gemm_wide_supported(int H, int I, int r_gu, int r_dn)
 
 hipError_t launch_gemm_wide(const GemmArgs &a, bool gated, hipStream_t s)
 {
-    const int blocks = a.n_tiles * a.n_slabs;
+    const int blocks = gemm_grid_blocks(a.n_tiles, a.n_slabs);
     if (blocks <= 0)
         return hipSuccess;
     if (gated)

@@ -38,6 +38,16 @@ struct PermuteArgs {
 // launch; the wide GEMM's direct loads read it in place of masked values.
 constexpr int kZeroBytes = 1024;
 
+// Blocks of a GEMM launch over n_tiles work-list entries (an upper bound)
+// and n_slabs column slabs: a multiple of 8, so that every (XCD, index) pair
+// the device-side work split uses exists (xcd_balanced_item hands XCD x the
+// items x * per .. x * per + per - 1, per = ceil(items / 8), to the blocks
+// x, x + 8, ..., which needs 8 * per blocks).
+inline int gemm_grid_blocks(int n_tiles, int n_slabs)
+{
+    return (n_tiles * n_slabs + 7) / 8 * 8;
+}
+
 // Upper bound on the GEMM work-list length for n slots and E_l experts.
 inline int max_gemm_tiles(int n, int E_l, int tile_rows)
 {

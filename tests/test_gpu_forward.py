@@ -35,6 +35,9 @@ TINY_AMP = CONFIGS["tiny"].replace(name="tiny_amp", sigma_lora_a=0.2, sigma_lora
 # without adapter leave some 16-row tiles out of the expand.
 WIDE = LayerConfig("wide", 700, 256, 192, 4, 2, 0, 4, 3, 24, 24, seed=35, mapping="uniform",
                    sigma_lora_a=0.1, sigma_lora_b=0.1)
+# hidden 128: the down GEMM has one column slab over 12 row tiles, a work list
+# whose length is not a multiple of the 8 XCDs (every item must still run)
+WIDE_H128 = WIDE.replace(name="wide_h128", hidden=128)
 # one rank-8 adapter (a single, mostly empty expand chunk), adapter in runs
 WIDE_R8 = WIDE.replace(name="wide_r8", num_tokens=520, num_loras=1, rank_gate_up=8,
                        rank_down=8, mapping="runs", run_length=130, seed=36,
@@ -73,7 +76,8 @@ def test_prefill_sampled_tokens():
     _compare(cfg, inp, got, tokens=toks)
 
 
-@pytest.mark.parametrize("cfg", [MID, MID_R64, MID_EP, BIG_ROWS, TINY_AMP, WIDE, WIDE_R8],
+@pytest.mark.parametrize("cfg", [MID, MID_R64, MID_EP, BIG_ROWS, TINY_AMP, WIDE, WIDE_R8,
+                                 WIDE_H128],
                          ids=lambda c: c.name)
 def test_small_shapes_and_lora_delta(cfg):
     announce(f"forward {cfg.name}")

@@ -244,12 +244,17 @@ int moe_lora_pack_weights(const moe_lora_shape *shape, const void *w13, const vo
  * `topk_ids` / `topk_weights` as they are (then routing->topk_ids
  * and routing->topk_weights are not written and may be NULL).  Every other
  * field of `routing` must be non-NULL.  `token_lora_mapping` as in
- * moe_lora_inputs.  Needs no workspace.
+ * moe_lora_inputs.  `workspace` is device memory of at least
+ * moe_lora_route_workspace_size(shape) bytes, 16-byte aligned (the permute's
+ * per-block histograms; its contents on entry do not matter); it may be NULL
+ * when that size is 0, i.e. for at most 1024 slots (T * k).
  */
+size_t moe_lora_route_workspace_size(const moe_lora_shape *shape);
+
 int moe_lora_route(const moe_lora_shape *shape, const float *router_logits,
                    const float *routing_bias, const int32_t *topk_ids, const float *topk_weights,
                    const int32_t *token_lora_mapping, const moe_lora_routing *routing,
-                   void *stream);
+                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * The layer forward.  Writes `out` bf16 [T, H] (16-byte aligned; NULL when

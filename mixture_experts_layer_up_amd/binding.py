@@ -85,7 +85,10 @@ def load_library(path: str = LIB_PATH):
     lib.moe_lora_packed_w2_bytes.restype = ctypes.c_size_t
     lib.moe_lora_pack_weights.argtypes = [P(Shape), vp, vp, vp, vp, vp]
     lib.moe_lora_pack_weights.restype = ctypes.c_int
-    lib.moe_lora_route.argtypes = [P(Shape), vp, vp, vp, vp, vp, P(Routing), vp]
+    lib.moe_lora_route_workspace_size.argtypes = [P(Shape)]
+    lib.moe_lora_route_workspace_size.restype = ctypes.c_size_t
+    lib.moe_lora_route.argtypes = [P(Shape), vp, vp, vp, vp, vp, P(Routing), vp,
+                                   ctypes.c_size_t, vp]
     lib.moe_lora_route.restype = ctypes.c_int
     lib.moe_lora_forward.argtypes = [P(Shape), P(Inputs), P(Routing), vp, vp, ctypes.c_size_t, vp]
     lib.moe_lora_forward.restype = ctypes.c_int
@@ -179,11 +182,17 @@ def route(shape: Shape, router_logits: Optional[torch.Tensor] = None,
           topk_ids: Optional[torch.Tensor] = None, topk_weights: Optional[torch.Tensor] = None,
           token_lora_mapping: Optional[torch.Tensor] = None,
           routing: Optional[Dict[str, torch.Tensor]] = None,
-          routing_bias: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+          routing_bias: Optional[torch.Tensor] = None,
+          workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     T, E, k = shape.num_tokens, shape.num_experts, shape.top_k
     dev = (router_logits if router_logits is not None else topk_ids).device
     r = routing if routing is not None else alloc_routing(shape, dev)
     rs = _routing_struct(r)
+    need = int(load_library().moe_lora_route_workspace_size(ctypes.byref(shape)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load_library().moe_lora_route(
         ctypes.byref(shape),
         _ptr(router_logits, torch.float32, (T, E), "router_logits"),
@@ -191,7 +200,7 @@ def route(shape: Shape, router_logits: Optional[torch.Tensor] = None,
         _ptr(topk_ids, torch.int32, (T, k), "topk_ids"),
         _ptr(topk_weights, torch.float32, (T, k), "topk_weights"),
         _ptr(token_lora_mapping, torch.int32, (T,), "token_lora_mapping"),
-        ctypes.byref(rs), _stream()))
+        ctypes.byref(rs), ws_ptr, ws_bytes, _stream()))
     return r
 
 

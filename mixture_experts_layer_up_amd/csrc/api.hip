@@ -67,7 +67,7 @@ bool lora_down_active(const moe_lora_shape *s) { return s->num_loras > 0 && s->r
 // Workspace regions; every offset is a multiple of 256 bytes.
 struct Layout {
     size_t ids, weights, counts, offsets, exp2perm, perm2exp, seg_offsets, seg_slots;
-    size_t tiles, tile_count, zeros, s_gu, act, s_dn, y, h;
+    size_t perm_scratch, tiles, tile_count, zeros, s_gu, act, s_dn, y, h;
     int tile_rows, max_tiles;
     size_t total;
 };
@@ -92,6 +92,7 @@ Layout make_layout(const moe_lora_shape *s)
     L.perm2exp = take(n * 4);
     L.seg_offsets = take((segs + 1) * 4);
     L.seg_slots = take(n * 4);
+    L.perm_scratch = take(permute_scratch_bytes((int)n, (int)el, s->num_loras));
     L.tile_rows = gemm_tile_rows((int)n, (int)el, s->hidden, s->inter,
                                  lora_gate_up_active(s) ? s->rank_gate_up : 0,
                                  lora_down_active(s) ? s->rank_down : 0);
@@ -123,9 +124,10 @@ struct RoutingPtrs {
     int32_t *counts, *offsets, *exp2perm, *perm2exp, *seg_offsets, *seg_slots;
 };
 
+// block_counts: permute_scratch_bytes of workspace (unused for one slot block)
 int enqueue_routing(const moe_lora_shape *s, const float *logits, const float *bias,
                     const int32_t *topk_ids, const int32_t *mapping, const RoutingPtrs &r,
-                    hipStream_t st,
+                    int32_t *block_counts, hipStream_t st,
                     int4 *tiles = nullptr, int tile_rows = 0, int max_tiles = 0,
                     int32_t *tile_count = nullptr, void *zeros = nullptr)
 {
@@ -153,6 +155,8 @@ int enqueue_routing(const moe_lora_shape *s, const float *logits, const float *b
     pa.max_tiles = max_tiles;
     pa.tile_count = tile_count;
     pa.zeros = static_cast<u32x4_t *>(zeros);
+    pa.G = permute_blocks(s->num_tokens * s->top_k);
+    pa.block_counts = block_counts;
     return check(launch_permute(pa, st));
 }
 
@@ -173,6 +177,7 @@ int enqueue_empty_batch(const moe_lora_shape *s, const moe_lora_routing *routing
     pa.expert_counts = routing->expert_counts;
     pa.expert_offsets = routing->expert_offsets;
     pa.seg_offsets = routing->lora_seg_offsets;
+    pa.G = 1;
     return check(launch_permute(pa, st));
 }
 
@@ -225,14 +230,29 @@ int moe_lora_pack_weights(const moe_lora_shape *shape, const void *w13, const vo
     return check(launch_pack(p2, st));
 }
 
+size_t moe_lora_route_workspace_size(const moe_lora_shape *shape)
+{
+    if (validate_shape(shape) != MOE_LORA_OK)
+        return 0;
+    return permute_scratch_bytes(shape->num_tokens * shape->top_k, shape->local_num_experts,
+                                 shape->num_loras);
+}
+
 int moe_lora_route(const moe_lora_shape *shape, const float *router_logits,
                    const float *routing_bias, const int32_t *topk_ids, const float *topk_weights,
                    const int32_t *token_lora_mapping, const moe_lora_routing *routing,
-                   void *stream)
+                   void *workspace, size_t workspace_bytes, void *stream)
 {
     MOE_TRY(validate_shape(shape));
     if (!routing)
         return MOE_LORA_ERR_INVALID_ARG;
+    const size_t need = moe_lora_route_workspace_size(shape);
+    if (need > 0 && !workspace)
+        return MOE_LORA_ERR_INVALID_ARG;
+    if (workspace_bytes < need)
+        return MOE_LORA_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(workspace, 16))
+        return MOE_LORA_ERR_MISALIGNED;
     if (shape->num_tokens == 0)
         return enqueue_empty_batch(shape, routing, static_cast<hipStream_t>(stream));
     const bool from_logits = router_logits != nullptr;
@@ -251,7 +271,7 @@ int moe_lora_route(const moe_lora_shape *shape, const float *router_logits,
                   routing->permuted_idx_to_expanded_idx, routing->lora_seg_offsets,
                   routing->lora_seg_slots};
     return enqueue_routing(shape, router_logits, routing_bias, topk_ids, token_lora_mapping, r,
-                           static_cast<hipStream_t>(stream));
+                           static_cast<int32_t *>(workspace), static_cast<hipStream_t>(stream));
 }
 
 int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
@@ -347,7 +367,8 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     void *zeros = ws + lay.zeros;
     int32_t *tile_count = reinterpret_cast<int32_t *>(ws + lay.tile_count);
     MOE_TRY(enqueue_routing(shape, in->router_logits, in->routing_bias, in->topk_ids,
-                            in->token_lora_mapping, r, st,
+                            in->token_lora_mapping, r,
+                            reinterpret_cast<int32_t *>(ws + lay.perm_scratch), st,
                             tiles, lay.tile_rows, lay.max_tiles, tile_count, zeros));
     MOE_TRY(record(ev, 1, st));
 

@@ -10,97 +10,97 @@
 // Reading taken here: inside one expert (and one virtual expert) slots keep
 // ascending slot order x = t * k + j, so the permutation is a stable counting
 // sort.  It is built without order-dependent atomics: LDS integer atomics
-// only produce counts (the same in any order), and ranks come from per-wave
-// prefix offsets plus a wave-local match mask built from ballots.
+// only produce counts (the same in any order), and ranks come from prefix
+// offsets plus a wave-local match mask built from ballots.
 //
-// Launch: two blocks of 1024 threads.  Block 0 sorts slots by local expert,
-// block 1 by virtual expert (adapter * E_l + local expert).
+// Two key types run side by side: blockIdx.y = 0 sorts slots by local expert,
+// blockIdx.y = 1 by virtual expert (adapter * E_l + local expert).  The slots
+// are cut into G = ceil(n / kPermuteSlotsPerBlock) consecutive blocks.  With G > 1 a
+// count kernel first writes every block's histogram to the workspace; the
+// rank kernel's blocks then each read the histograms, scan the totals into
+// the offsets (every block the same, redundantly) and rank their own slots:
+// position = offset of the key + slots of the key in earlier blocks + in
+// earlier waves of the block + in earlier 64-slot groups of the wave + lower
+// lanes of the group with the same key.  With G == 1 the rank kernel's own
+// histogram is the whole one and the count kernel is skipped.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace moe_lora {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kMaxKeys = 8192;   // local experts, or adapters * local experts
-constexpr int kTable = 8192;     // per-wave running offsets, waves * keys
-constexpr int kKeyCache = 16384; // slot keys kept in LDS when n fits
+constexpr int kIters = kPermuteSlotsPerBlock / kThreads;  // 64-slot groups per wave, at most
+constexpr int kMaxKeys = 8192;                            // local experts, or adapters * local experts
+constexpr int kMaxExperts = 1024;
 
-__device__ __forceinline__ int slot_key(const PermuteArgs &a, bool by_segment, int x)
+// key of a slot from its expert id and its token's adapter l (-1: none)
+__device__ __forceinline__ int key_from(const PermuteArgs &a, bool by_segment, int id, int l)
 {
-    const int id = a.topk_ids[x];
     if (id < a.off || id >= a.off + a.E_l)
         return -1;  // not local: another expert-parallel shard owns it
     const int le = id - a.off;
     if (!by_segment)
         return le;
-    const int l = a.mapping ? a.mapping[x / a.k] : -1;
     if (l < 0 || l >= a.L)
         return -1;  // token without adapter
     return l * a.E_l + le;
 }
 
-__global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a)
+// row stride of the per-block histograms in the workspace (int4 loads)
+__device__ __forceinline__ int round4(int v) { return (v + 3) & ~3; }
+
+struct BlockSlots {
+    int beg, end;  // the block's slots
+    int chunk;     // slots per wave: 64 * groups
+    int groups;    // 64-slot groups per wave (uniform)
+};
+
+__device__ __forceinline__ BlockSlots block_slots(int n, int g)
 {
-    __shared__ int hist[kMaxKeys + 1];
-    __shared__ int table[kTable];
-    __shared__ int wave_excl[kWaves];
-    __shared__ int tile_excl[kWaves];
-    __shared__ int tile_total;
-    __shared__ int key_cache[kKeyCache];
+    BlockSlots b;
+    b.beg = g * kPermuteSlotsPerBlock;
+    b.end = min(n, b.beg + kPermuteSlotsPerBlock);
+    const int nb = max(0, b.end - b.beg);
+    b.groups = (nb + kThreads - 1) / kThreads;
+    b.chunk = b.groups * kWave;
+    return b;
+}
 
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid >> 6;
-    const bool by_segment = blockIdx.x == 1;
-    const int n = a.T * a.k;
-    const int NK = by_segment ? a.L * a.E_l : a.E_l;
-    int32_t *out_offsets = by_segment ? a.seg_offsets : a.expert_offsets;
-    int32_t *out_list = by_segment ? a.seg_slots : a.perm2exp;
-    if (!by_segment && a.zeros && tid < kZeroBytes / 16)
-        a.zeros[tid] = u32x4_t{0u, 0u, 0u, 0u};
-
-    if (NK == 0) {  // no adapters: empty segment list
-        if (tid == 0)
-            out_offsets[0] = 0;
-        for (int i = tid; i < n; i += kThreads)
-            out_list[i] = -1;
-        return;
+// The keys of this lane's slots: group i holds slot beg + wave * chunk +
+// 64 i + lane (-1 past the block or the wave's chunk).  All loads are issued
+// before any is used.
+__device__ __forceinline__ void load_keys(const PermuteArgs &a, bool by_segment,
+                                          const BlockSlots &b, int wave, int lane,
+                                          int (&key)[kIters])
+{
+    int id[kIters], l[kIters];
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+        id[i] = -1;
+        l[i] = -1;
+        if (i >= b.groups)  // uniform
+            break;
+        const int x = b.beg + wave * b.chunk + i * kWave + lane;
+        if (x < b.end) {
+            id[i] = a.topk_ids[x];
+            if (by_segment && a.mapping)
+                l[i] = a.mapping[x / a.k];
+        }
     }
-
-    // 0. every slot's key, once: into LDS when the batch fits (independent
-    // loads, so they are all in flight together), else recomputed per pass
-    const bool cached = n <= kKeyCache;
-    if (cached) {
-        for (int x = tid; x < n; x += kThreads)
-            key_cache[x] = slot_key(a, by_segment, x);
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+        const int x = b.beg + wave * b.chunk + i * kWave + lane;
+        key[i] = (i < b.groups && x < b.end) ? key_from(a, by_segment, id[i], l[i]) : -1;
     }
-    auto key_of = [&](int x) { return cached ? key_cache[x] : slot_key(a, by_segment, x); };
+}
 
-    // 1. histogram
-    for (int i = tid; i <= NK; i += kThreads)
-        hist[i] = 0;
-    __syncthreads();
-    for (int x = tid; x < n; x += kThreads) {
-        const int key = key_of(x);
-        if (key >= 0)
-            atomicAdd(&hist[key], 1);
-    }
-    __syncthreads();
-
-    // 2. exclusive scan: each thread owns a contiguous run of keys
-    const int per = (NK + kThreads - 1) / kThreads;
-    const int beg = min(NK, tid * per);
-    const int end = min(NK, beg + per);
-    int local = 0;
-    for (int i = beg; i < end; ++i) {
-        const int c = hist[i];
-        if (!by_segment)
-            a.expert_counts[i] = c;
-        local += c;
-    }
-    int incl = local;
+// Inclusive scan of one value per thread over the block; also the block total.
+// Uses wave_tot[kWaves]; all threads must call it.
+__device__ __forceinline__ int block_scan(int v, int lane, int wave, int *wave_tot, int &total)
+{
+    int incl = v;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
         const int o = __shfl_up(incl, off);
@@ -108,142 +108,228 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a)
             incl += o;
     }
     if (lane == kWave - 1)
-        wave_excl[wave] = incl;
+        wave_tot[wave] = incl;
     __syncthreads();
-    if (wave == 0) {
-        const int ws = lane < kWaves ? wave_excl[lane] : 0;
-        int wi = ws;
+    int before = 0;
+    total = 0;
 #pragma unroll
-        for (int off = 1; off < kWaves; off <<= 1) {
-            const int o = __shfl_up(wi, off);
-            if (lane >= off)
-                wi += o;
+    for (int w = 0; w < kWaves; ++w) {
+        const int t = wave_tot[w];
+        before += w < wave ? t : 0;
+        total += t;
+    }
+    __syncthreads();  // wave_tot is reused by the next call
+    return incl + before;
+}
+
+__global__ __launch_bounds__(kThreads) void permute_count_kernel(PermuteArgs a)
+{
+    __shared__ int hist[kMaxKeys];
+    const bool by_segment = blockIdx.y == 1;
+    const int NK = by_segment ? a.L * a.E_l : a.E_l;
+    if (NK == 0)
+        return;
+    const int g = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x >> 6;
+    const int n = a.T * a.k;
+    const BlockSlots b = block_slots(n, g);
+    int key[kIters];
+    load_keys(a, by_segment, b, wave, lane, key);
+    for (int j = threadIdx.x; j < NK; j += kThreads)
+        hist[j] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kIters; ++i)
+        if (key[i] >= 0)
+            atomicAdd(&hist[key[i]], 1);
+    __syncthreads();
+    const int NKs = round4(NK);
+    int32_t *dst = a.block_counts + (by_segment ? (size_t)a.G * round4(a.E_l) : 0) + (size_t)g * NKs;
+    for (int j = threadIdx.x; j < NKs; j += kThreads)
+        dst[j] = j < NK ? hist[j] : 0;
+}
+
+__global__ __launch_bounds__(kThreads) void permute_rank_kernel(PermuteArgs a)
+{
+    __shared__ int table[kWaves * kMaxKeys];  // per-wave counts, then per-wave running positions
+    __shared__ int exp_first[kMaxExperts];    // expert offsets and counts, for the work list
+    __shared__ int exp_rows[kMaxExperts];
+    __shared__ int wave_tot[kWaves];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid >> 6;
+    const bool by_segment = blockIdx.y == 1;
+    const int g = blockIdx.x;
+    const int G = a.G;
+    const int n = a.T * a.k;
+    const int NK = by_segment ? a.L * a.E_l : a.E_l;
+    int32_t *out_offsets = by_segment ? a.seg_offsets : a.expert_offsets;
+    int32_t *out_list = by_segment ? a.seg_slots : a.perm2exp;
+    const BlockSlots b = block_slots(n, g);
+    const bool lead = g == 0;  // writes the per-key arrays and the work list
+    if (lead && !by_segment && a.zeros && tid < kZeroBytes / 16)
+        a.zeros[tid] = u32x4_t{0u, 0u, 0u, 0u};
+
+    if (NK == 0) {  // no adapters: empty segment list
+        if (lead && tid == 0)
+            out_offsets[0] = 0;
+        for (int x = b.beg + tid; x < b.end; x += kThreads)
+            out_list[x] = -1;
+        return;
+    }
+
+    int key[kIters];
+    load_keys(a, by_segment, b, wave, lane, key);
+
+    // 1. per-wave histograms of the block's slots
+    for (int j = tid; j < kWaves * NK; j += kThreads)
+        table[j] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kIters; ++i)
+        if (key[i] >= 0)
+            atomicAdd(&table[wave * NK + key[i]], 1);
+    __syncthreads();
+
+    // 2. totals per key, their exclusive scan (the offsets), and each wave's
+    // first position per key.  Keys in rows of 4 * kThreads, four consecutive
+    // keys per thread, so that the other blocks' histograms (written by the
+    // count kernel, mostly in other XCDs' caches) come in as int4 loads, 16
+    // blocks' rows per batch, all in flight together.
+    const int NKs = round4(NK);
+    const int32_t *counts = a.block_counts + (by_segment ? (size_t)G * round4(a.E_l) : 0);
+    int carry = 0;
+    for (int j0 = 0; j0 < NK; j0 += 4 * kThreads) {
+        const int jb = j0 + 4 * tid;
+        int before[4] = {0, 0, 0, 0}, after[4] = {0, 0, 0, 0};
+        if (G > 1 && jb < NK) {
+            for (int q0 = 0; q0 < G; q0 += 16) {
+                int4 c[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {  // clamped rows: in bounds, counted only if real
+                    const int q = min(q0 + u, G - 1);
+                    c[u] = *reinterpret_cast<const int4 *>(counts + (size_t)q * NKs + jb);
+                }
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const int q = q0 + u;
+                    const bool lo = q < g, hi = q > g && q < G;
+                    before[0] += lo ? c[u].x : 0;
+                    before[1] += lo ? c[u].y : 0;
+                    before[2] += lo ? c[u].z : 0;
+                    before[3] += lo ? c[u].w : 0;
+                    after[0] += hi ? c[u].x : 0;
+                    after[1] += hi ? c[u].y : 0;
+                    after[2] += hi ? c[u].z : 0;
+                    after[3] += hi ? c[u].w : 0;
+                }
+            }
         }
-        if (lane < kWaves)
-            wave_excl[lane] = wi - ws;
+        int wc[4][kWaves], total[4];
+        int mine = 0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int j = jb + m;
+            const bool valid = j < NK;
+            int in_block = 0;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                wc[m][w] = valid ? table[w * NK + j] : 0;
+                in_block += wc[m][w];
+            }
+            total[m] = valid ? before[m] + in_block + after[m] : 0;
+            mine += total[m];
+        }
+        int row_total;
+        const int incl = block_scan(mine, lane, wave, wave_tot, row_total);
+        int off = carry + incl - mine;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int j = jb + m;
+            if (j < NK) {
+                int run = off + before[m];
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) {
+                    table[w * NK + j] = run;
+                    run += wc[m][w];
+                }
+                if (lead) {
+                    out_offsets[j] = off;
+                    if (!by_segment) {
+                        a.expert_counts[j] = total[m];
+                        exp_first[j] = off;
+                        exp_rows[j] = total[m];
+                    }
+                }
+            }
+            off += total[m];
+        }
+        carry += row_total;
     }
-    __syncthreads();
-    int run = wave_excl[wave] + incl - local;
-    for (int i = beg; i < end; ++i) {
-        const int c = hist[i];
-        hist[i] = run;
-        out_offsets[i] = run;
-        run += c;
-    }
-    if (tid == kThreads - 1) {  // its run ends at the grand total
-        hist[NK] = run;
-        out_offsets[NK] = run;
-    }
-    __syncthreads();
-    const int total = hist[NK];
-    for (int i = total + tid; i < n; i += kThreads)
-        out_list[i] = -1;
+    const int grand = carry;  // slots with a key
+    if (lead && tid == 0)
+        out_offsets[NK] = grand;
+    for (int x = max(grand, b.beg) + tid; x < b.end; x += kThreads)
+        out_list[x] = -1;  // past the keyed slots
 
     // GEMM work list: chunks of at most tile_rows rows per expert, in expert
-    // order.  Same run-per-thread scan as above, over ceil(count / tile_rows).
-    if (!by_segment && a.tiles) {
-        int tl = 0;
-        for (int i = beg; i < end; ++i) {
-            const int c = (i + 1 < NK ? hist[i + 1] : total) - hist[i];
-            tl += (c + a.tile_rows - 1) / a.tile_rows;
+    // order; every chunk of expert e carries e's whole row range and the
+    // index of e's first chunk
+    if (lead && !by_segment && a.tiles) {
+        __syncthreads();  // exp_first / exp_rows
+        int tcarry = 0;
+        for (int j0 = 0; j0 < NK; j0 += kThreads) {
+            const int j = j0 + tid;
+            const int rows = j < NK ? exp_rows[j] : 0;
+            const int nt = (rows + a.tile_rows - 1) / a.tile_rows;
+            int row_total;
+            const int incl = block_scan(nt, lane, wave, wave_tot, row_total);
+            const int t0 = tcarry + incl - nt;
+            for (int r = 0; r < nt; ++r)
+                a.tiles[t0 + r] = make_int4(j, exp_first[j], rows, t0);
+            tcarry += row_total;
         }
-        int ti = tl;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int o = __shfl_up(ti, off);
-            if (lane >= off)
-                ti += o;
-        }
-        if (lane == kWave - 1)
-            tile_excl[wave] = ti;
-        __syncthreads();
-        if (wave == 0) {
-            const int ws = lane < kWaves ? tile_excl[lane] : 0;
-            int wi = ws;
-#pragma unroll
-            for (int off = 1; off < kWaves; off <<= 1) {
-                const int o = __shfl_up(wi, off);
-                if (lane >= off)
-                    wi += o;
-            }
-            if (lane < kWaves)
-                tile_excl[lane] = wi - ws;
-        }
-        __syncthreads();
-        int t0 = tile_excl[wave] + ti - tl;
-        for (int i = beg; i < end; ++i) {
-            const int first = hist[i];
-            const int c = (i + 1 < NK ? hist[i + 1] : total) - first;
-            const int tb = t0;  // every tile of expert i carries the expert's whole range
-            for (int r = 0; r < c; r += a.tile_rows)
-                a.tiles[t0++] = make_int4(i, first, c, tb);
-        }
-        if (tid == kThreads - 1) {  // t0 is now the number of tiles
-            tile_total = t0;
-            if (a.tile_count)
-                *a.tile_count = t0;
-        }
-        __syncthreads();
-        for (int i = tile_total + tid; i < a.max_tiles; i += kThreads)
+        if (tid == 0 && a.tile_count)
+            *a.tile_count = tcarry;
+        for (int i = tcarry + tid; i < a.max_tiles; i += kThreads)
             a.tiles[i] = make_int4(-1, 0, 0, 0);
     }
+    __syncthreads();  // table holds the running positions
 
-    // 3. stable ranks: split the slots into W contiguous chunks, one per wave
-    const int W = max(1, min(kWaves, kTable / NK));
-    const int chunk = (n + W - 1) / W;
-    for (int i = tid; i < W * NK; i += kThreads)
-        table[i] = 0;
-    __syncthreads();
-    if (wave < W) {
-        const int cb = wave * chunk;
-        const int ce = min(n, cb + chunk);
-        for (int x = cb + lane; x < ce; x += kWave) {
-            const int key = key_of(x);
-            if (key >= 0)
-                atomicAdd(&table[wave * NK + key], 1);
+    // 3. stable ranks, one 64-slot group at a time per wave
+    volatile int *tab = table + wave * NK;
+    const int nbits = NK > 1 ? 32 - __clz(NK - 1) : 0;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+        if (i >= b.groups)  // uniform
+            break;
+        const int x = b.beg + wave * b.chunk + i * kWave + lane;
+        const int k = key[i];
+        unsigned long long same = __ballot(k >= 0);
+        for (int bit = 0; bit < nbits; ++bit) {
+            const bool v = (k >> bit) & 1;
+            const unsigned long long bb = __ballot(v);
+            same &= v ? bb : ~bb;
         }
-    }
-    __syncthreads();
-    for (int key = tid; key < NK; key += kThreads) {  // offsets of each wave's first slot per key
-        int r = hist[key];
-        for (int w = 0; w < W; ++w) {
-            const int c = table[w * NK + key];
-            table[w * NK + key] = r;
-            r += c;
-        }
-    }
-    __syncthreads();
-    if (wave < W) {
-        const int cb = wave * chunk;
-        const int ce = min(n, cb + chunk);
-        volatile int *tab = table + wave * NK;
-        const int nbits = NK > 1 ? 32 - __clz(NK - 1) : 0;
-        const unsigned long long lt = (1ull << lane) - 1ull;
-        for (int base = cb; base < ce; base += kWave) {
-            const int x = base + lane;
-            const int key = x < ce ? key_of(x) : -1;
-            unsigned long long same = __ballot(key >= 0);
-            for (int b = 0; b < nbits; ++b) {
-                const bool bit = (key >> b) & 1;
-                const unsigned long long bb = __ballot(bit);
-                same &= bit ? bb : ~bb;
-            }
-            if (key >= 0) {
-                const int pos = tab[key] + __popcll(same & lt);
-                if (by_segment) {
+        const int pos = k >= 0 ? tab[k] + __popcll(same & lt) : -1;
+        const bool placed = k >= 0 && pos < n;  // always, for consistent inputs; guards the store
+        if (x < b.end) {
+            if (by_segment) {
+                if (placed)
                     a.seg_slots[pos] = x;
-                } else {
+            } else {
+                a.exp2perm[x] = pos;
+                if (placed)
                     a.perm2exp[pos] = x;
-                    a.exp2perm[x] = pos;
-                }
-            } else if (!by_segment && x < ce) {
-                a.exp2perm[x] = -1;
             }
-            // LDS operations of one wave complete in issue order, so every
-            // lane's read above precedes this update by the group's last lane.
-            if (key >= 0 && (same >> lane) == 1ull)
-                tab[key] = tab[key] + __popcll(same);
         }
+        // LDS operations of one wave complete in issue order, so every
+        // lane's read above precedes this update by the group's last lane.
+        if (k >= 0 && (same >> lane) == 1ull)
+            tab[k] = tab[k] + __popcll(same);
     }
 }
 
@@ -251,7 +337,10 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a)
 
 hipError_t launch_permute(const PermuteArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL(permute_kernel, dim3(2), dim3(kThreads), 0, s, a);
+    const int G = a.G;
+    if (G > 1)
+        hipLaunchKernelGGL(permute_count_kernel, dim3(G, 2), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(permute_rank_kernel, dim3(G, 2), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -65,7 +65,7 @@ def test_invalid_shapes_rejected(lib, field, value):
     shape = binding.make_shape(cfg)
     rs = binding.Routing()
     assert lib.moe_lora_route(ctypes.byref(shape), ctypes.c_void_p(256), None, None, None,
-                              None, ctypes.byref(rs), None) == ERR_SHAPE
+                              None, ctypes.byref(rs), None, 0, None) == ERR_SHAPE
 
 
 def _fake(addr=4096):
@@ -131,9 +131,9 @@ def test_route_and_pack_validation(lib):
     shape = binding.make_shape(CONFIGS["tiny"])
     rs = binding.Routing()   # all NULL
     assert lib.moe_lora_route(ctypes.byref(shape), _fake(), None, None, None, None,
-                              ctypes.byref(rs), None) == ERR_INVALID_ARG
+                              ctypes.byref(rs), None, 0, None) == ERR_INVALID_ARG
     assert lib.moe_lora_route(ctypes.byref(shape), None, None, None, None, None,
-                              None, None) == ERR_INVALID_ARG
+                              None, None, 0, None) == ERR_INVALID_ARG
     assert lib.moe_lora_pack_weights(ctypes.byref(shape), None, _fake(), _fake(), _fake(),
                                      None) == ERR_INVALID_ARG
     assert lib.moe_lora_pack_weights(ctypes.byref(shape), _fake(4097), _fake(), _fake(),
@@ -197,4 +197,31 @@ def test_routing_method_validation(lib):
     assert binding.workspace_size(shape) == 0
     rs = _routing_fake()
     assert lib.moe_lora_route(ctypes.byref(shape), _fake(), None, None, None, None,
-                              ctypes.byref(rs), None) == ERR_INVALID_ARG
+                              ctypes.byref(rs), None, 0, None) == ERR_INVALID_ARG
+
+
+def test_route_workspace_size_and_validation(lib):
+    """moe_lora_route needs workspace only for more than one permute block
+    (1024 slots): G = ceil(T * k / 1024) histograms of E_l and L * E_l counts,
+    each row padded to a multiple of 4."""
+    small = binding.make_shape(CONFIGS["decode64"])          # 512 slots
+    assert lib.moe_lora_route_workspace_size(ctypes.byref(small)) == 0
+    cfg = CONFIGS["prefill"]                                 # 16384 slots
+    big = binding.make_shape(cfg)
+    G = cfg.num_tokens * cfg.top_k // 1024
+    E_l, L = cfg.local_num_experts, cfg.num_loras
+    need = G * (E_l + L * E_l) * 4
+    assert lib.moe_lora_route_workspace_size(ctypes.byref(big)) == need
+    odd = binding.make_shape(cfg.replace(local_num_experts=5, num_experts=128, num_loras=3))
+    assert lib.moe_lora_route_workspace_size(ctypes.byref(odd)) == G * (8 + 16) * 4
+    # the forward workspace holds it too
+    assert binding.workspace_size(big) > need
+    rs = _routing_fake()
+    assert lib.moe_lora_route(ctypes.byref(big), _fake(), None, None, None, None,
+                              ctypes.byref(rs), None, 0, None) == ERR_INVALID_ARG
+    assert lib.moe_lora_route(ctypes.byref(big), _fake(), None, None, None, None,
+                              ctypes.byref(rs), _fake(1 << 20), need - 4, None) == ERR_WS
+    assert lib.moe_lora_route(ctypes.byref(big), _fake(), None, None, None, None,
+                              ctypes.byref(rs), _fake((1 << 20) + 4), need, None) == ERR_ALIGN
+    bad = binding.make_shape(cfg.replace(top_k=0))
+    assert lib.moe_lora_route_workspace_size(ctypes.byref(bad)) == 0

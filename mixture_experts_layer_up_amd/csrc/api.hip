@@ -415,8 +415,10 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     g1.k = k;
     g1.I = I;
     g1.Y = act;
-    // column slabs per expert: 64 columns (decode kernel) or 128 (wide kernel)
-    auto slabs = [&](int NT) { return lay.tile_rows == kDecodeTileRows ? NT / 4 : NT / 8; };
+    // column slabs per expert: 64 columns (decode kernel) or 256 (wide kernel)
+    auto slabs = [&](int NT) {
+        return lay.tile_rows == kDecodeTileRows ? NT / 4 : gemm_wide_slabs(NT);
+    };
     g1.n_slabs = slabs(g1.NT);
     g1.zeros = static_cast<const uint16_t *>(zeros);
     if (two_stream) {

@@ -35,6 +35,9 @@
 //  * Every load in the pipeline is issued unconditionally (indices clamped,
 //    values masked afterwards) so all paths have the same number of
 //    outstanding loads and the compiler's wait counts stay exact.
+#include <algorithm>
+#include <cmath>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -476,8 +479,17 @@ hipError_t launch_gemm_variant(const GemmArgs &a, hipStream_t s)
 int gemm_tile_rows(int n_slots, int E_l, int H, int I, int r_gu, int r_dn)
 {
     // the wide kernel once experts average 32 or more rows
-    return (n_slots >= 32 * E_l && gemm_wide_supported(H, I, r_gu, r_dn)) ? kWideTileRows
-                                                                          : kDecodeTileRows;
+    if (n_slots < 32 * E_l || !gemm_wide_supported(H, I, r_gu, r_dn))
+        return kDecodeTileRows;
+    // Every wide work item streams a whole 128-column weight slab whatever
+    // its rows, so a launch costs about ceil(items / resident blocks) item
+    // times: an expert split over two tiles adds a nearly empty item per
+    // slab, and a few of those start a whole extra round.  Tiles therefore
+    // cover the mean rows per expert plus four standard deviations of a
+    // Poisson count (rounded up to 16), up to the kernel's maximum.
+    const double mean = (double)n_slots / E_l;
+    const int want = (int)std::ceil(mean + 4.0 * std::sqrt(mean));
+    return std::min(kWideMaxTileRows, (want + 15) / 16 * 16);
 }
 
 hipError_t launch_gemm_gate_up(const GemmArgs &a, hipStream_t s)

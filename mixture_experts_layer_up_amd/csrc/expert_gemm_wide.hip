@@ -7,40 +7,49 @@
 // "Files changed" table, launcher row, and Flow section 2.
 //
 // Design for gfx950 when rows per expert are many:
-//  * One block = 4 waves = one (row tile of at most 160 rows of one expert,
-//    128-column slab).  The waves split N: wave w owns column tiles 2w and
-//    2w + 1 of the slab (for gate_up a matching gate/up pair), so all four
-//    waves multiply the same activation rows and no cross-wave reduction is
-//    needed.
-//  * Operands reach LDS by direct global->LDS loads (global_load_lds_dwordx4):
-//    no register staging and no LDS store instructions.  Four K chunks of 32
-//    are resident (18 KiB each: 160 activation rows + the slab's 8 weight
-//    fragments); three are in flight while the fourth is multiplied.  The
-//    wait for a chunk is an explicit vmcnt on the issuing wave followed by a
-//    block barrier, so weight and activation loads stream continuously.
+//  * One block = 8 waves = one (row tile of at most 176 rows of one expert,
+//    256-column slab), one block per CU.  Waves 0-3 are consumers: consumer
+//    w owns the slab's 64-column group w (for gate_up two gate/up pairs) for
+//    all 176 rows, and only reads LDS and issues MFMAs.  Waves 4-7 are
+//    producers: they only compute addresses and issue the direct
+//    global->LDS loads (global_load_lds_dwordx4), which occupy the issuing
+//    wave for a long time each; on separate waves that time no longer delays
+//    any MFMA.
+//  * K advances in chunks of 32.  kStages chunks are resident in LDS (27 KiB
+//    each: 176 activation rows + the slab's 16 weight fragments); the
+//    producers keep kStages - 1 in flight.  One block barrier per chunk both
+//    publishes a landed chunk (each producer waits for its own loads with an
+//    explicit vmcnt first) and frees the stage the consumers finished.
 //  * Activation rows are stored 64 bytes apart with the four 16-byte K
 //    quarters of a row XOR-swizzled by bits 1..3 of the row, so the 16-row
 //    MFMA fragment reads hit distinct LDS banks; a direct load writes 1 KiB
-//    contiguously, which is bank-conflict free by construction.
+//    contiguously, which is bank-conflict free by construction.  Rows of M
+//    tiles past the tile are not loaded at all.
 //  * LoRA expand chunks follow the main K chunks.  A row's expand values are
 //    kept only in the K block of its own adapter: other lanes load from a
 //    zero block in the workspace instead (a direct load cannot mask).  An M
 //    tile (16 rows) skips the MFMAs of a chunk whose adapters it does not
 //    contain.  Needs rank % 8 == 0 (16-byte expand rows).
 //  * MFMA guards are scalar (wave-uniform) branches: MFMA ignores EXEC.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
 namespace moe_lora {
 namespace {
 
-constexpr int kWMT = 10;                       // M tiles of 16 rows per block
-constexpr int kWRows = kWMT * 16;              // 160 rows
-constexpr int kStages = 4;                     // K chunks resident in LDS
-constexpr int kAStageBytes = kWRows * 64;      // 160 rows x 32 bf16
-constexpr int kBStageBytes = 8 * 1024;         // 8 MFMA B fragments
+constexpr int kWMT = kWideMaxTileRows / 16;    // M tiles of 16 rows per block: 11
+constexpr int kWRows = kWMT * 16;              // 176 rows
+constexpr int kCons = 4;                       // consumer waves
+constexpr int kNTW = 4;                        // 16-column tiles per consumer
+constexpr int kSlabCols = kCons * kNTW * 16;   // 256 columns per block
+constexpr int kThreadsW = 2 * kCons * kWave;   // consumers + producers
+constexpr int kStages = 5;                     // K chunks resident in LDS
+constexpr int kAStageBytes = kWRows * 64;      // 176 rows x 32 bf16
+constexpr int kBStageBytes = kCons * kNTW * 1024;  // 16 MFMA B fragments
 constexpr int kStageBytes = kAStageBytes + kBStageBytes;
-constexpr int kAInstr = kWRows / 16;           // 1 KiB direct loads per A stage
+constexpr int kAPerProd = (kWMT + kCons - 1) / kCons;  // A loads per producer: 3
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -73,9 +82,10 @@ __device__ __forceinline__ void load_lds16_stream(const void *g, uint32_t lds_ad
 __device__ __forceinline__ int a_swizzle(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 
 // Wait until at most N of this wave's vector loads are outstanding and its
-// LDS reads are done, then synchronise the block.  The direct loads write
-// LDS behind the compiler's back, so this wait is spelled out; the empty asm
-// statements keep LDS reads from moving across the barrier.
+// LDS reads are done, then synchronise the block (N = 63: LDS reads only).
+// The direct loads write LDS behind the compiler's back, so this wait is
+// spelled out; the empty asm statements keep LDS reads from moving across
+// the barrier.
 template <int N>
 __device__ __forceinline__ void dma_wait_barrier()
 {
@@ -93,14 +103,12 @@ __device__ __forceinline__ void dma_drain()
 }
 
 template <bool kGated>
-__global__ __launch_bounds__(256, 2) void expert_gemm_wide_kernel(GemmArgs a)
+__global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs a)
 {
     __shared__ __align__(1024) unsigned char smem[kStages * kStageBytes];
-    auto stage = [&](int st) -> unsigned char * { return smem + st * kStageBytes; };
     // LDS byte address of smem, for the direct loads (M0)
     const uint32_t smem_lds =
         __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_void *)smem));
-    auto stage_lds = [&](int st) { return smem_lds + (uint32_t)(st * kStageBytes); };
     __shared__ int row_x[kWRows];
     __shared__ int row_src[kWRows];
     __shared__ int row_adapter[kWRows];
@@ -110,7 +118,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_wide_kernel(GemmArgs a)
     const int lane = tid & (kWave - 1);
     const int wave = wave_id();
 
-    // work item -> (expert, 128-column slab, row tile); see expert_gemm.hip
+    // work item -> (expert, 256-column slab, row tile); see expert_gemm.hip
     const int logical = xcd_balanced_item(blockIdx.x, *a.tile_count * a.n_slabs);
     if (logical < 0)
         return;
@@ -136,7 +144,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_wide_kernel(GemmArgs a)
 
     // rows of this tile: slot, source row, adapter (rows past the tile
     // repeat the last row and carry no adapter)
-    for (int r = tid; r < kWRows; r += 256) {
+    for (int r = tid; r < kWRows; r += kThreadsW) {
         const int p = row0 + min(r, n_rows - 1);
         const int x = a.perm2exp[p];
         const int tok = x / a.k;
@@ -153,119 +161,162 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_wide_kernel(GemmArgs a)
                 m |= 1ull << row_adapter[r];
         mt_adapters[tid] = m;
     }
+    lds_barrier();  // mt_adapters
 
-    // Activation loads of this wave: A instructions j = wave + 4 i (waves 0
-    // and 1 issue three, waves 2 and 3 two).  Lane `lane` of instruction j
-    // fills physical row 16 j + lane / 4, physical quarter lane % 4, which
-    // holds logical quarter (lane % 4) ^ swizzle(row).
-    constexpr int kAPerWave = (kAInstr + 3) / 4;  // 3
-    const int n_ai = (kAInstr - wave + 3) / 4;    // 3, 3, 2, 2 (uniform)
-    const uint16_t *a_src[kAPerWave];
-    int a_x[kAPerWave], a_ad[kAPerWave], a_q[kAPerWave];
-#pragma unroll
-    for (int i = 0; i < kAPerWave; ++i) {
-        const int j = min(wave + 4 * i, kAInstr - 1);
-        const int pr = 16 * j + (lane >> 2);
-        const int q = (lane & 3) ^ a_swizzle(pr);
-        a_src[i] = a.X + (size_t)row_src[pr] * a.K + q * 8;
-        a_x[i] = row_x[pr];
-        a_ad[i] = row_adapter[pr];
-        a_q[i] = q;
-    }
-    // Weight loads of this wave: its own two fragments t0, t0 + 1 of packed
-    // 64-column slab s64 (instructions 2 wave, 2 wave + 1 of the B stage).
-    const int s64 = slab * 2 + (wave >> 1);
-    const int t0 = (wave & 1) * 2;
-    const uint16_t *b_main =
-        a.Wp + (((size_t)le * (a.n_slabs * 2) + s64) * (size_t)KC * 4 + t0) * 512 + lane * 8;
-    int b_col[2];
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-        const int nt16 = s64 * 4 + t0 + n;
-        b_col[n] = kGated ? (nt16 & 1) * a.I + (nt16 >> 1) * 16 + (lane & 15)
-                          : nt16 * 16 + (lane & 15);
-    }
-    const uint16_t *zeros = a.zeros;
+    // The 64-column group g (0..3) of this slab: packed 64-column weight
+    // slab s64, present when it lies inside the N columns.
+    const int NS64 = a.NT >> 2;
+    const int g = wave & (kCons - 1);
+    const int s64 = slab * kCons + g;
+    const bool has_cols = s64 < NS64;
 
-    // issue the direct loads of chunk vc into LDS stage st
-    auto issue_main = [&](int vc, int st) {
-        const uint32_t sa = stage_lds(st);
-        const uint32_t sb = sa + kAStageBytes;
+    if (wave >= kCons) {
+        // ------------------------------------------------------------ producer
+        // A loads: M tiles j = g + 4 i that exist.  Lane `lane` of the load of
+        // M tile j fills physical row 16 j + lane / 4, physical quarter
+        // lane % 4, which holds logical quarter (lane % 4) ^ swizzle(row).
+        const int n_a = max(0, min(kAPerProd, (n_mt - g + kCons - 1) / kCons));
+        const uint16_t *a_src[kAPerProd];
+        int a_x[kAPerProd], a_ad[kAPerProd], a_q[kAPerProd];
 #pragma unroll
-        for (int i = 0; i < kAPerWave; ++i)
-            if (i < n_ai)
-                load_lds16(a_src[i] + vc * 32, sa + (wave + 4 * i) * 1024);
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-            load_lds16_stream(b_main + ((size_t)vc * 4 + n) * 512, sb + (2 * wave + n) * 1024);
-    };
-    auto issue = [&](int vc, int st) {
-        if (vc < KC) {
-            issue_main(vc, st);
-            return;
+        for (int i = 0; i < kAPerProd; ++i) {
+            const int j = min(g + kCons * i, kWMT - 1);
+            const int pr = 16 * j + (lane >> 2);
+            const int q = (lane & 3) ^ a_swizzle(pr);
+            a_src[i] = a.X + (size_t)row_src[pr] * a.K + q * 8;
+            a_x[i] = row_x[pr];
+            a_ad[i] = row_adapter[pr];
+            a_q[i] = q;
         }
-        const uint32_t sa = stage_lds(st);
-        const uint32_t sb = sa + kAStageBytes;
-        const int c = vc - KC;
+        // B loads: the four fragments of weight slab s64 (contiguous 4 KiB
+        // per chunk), or of the LoRA B columns of its four 16-column tiles
+        const uint16_t *b_main =
+            a.Wp + ((size_t)le * NS64 + min(s64, NS64 - 1)) * (size_t)KC * 4 * 512 + lane * 8;
+        int b_col[kNTW];
 #pragma unroll
-        for (int i = 0; i < kAPerWave; ++i) {
-            if (i < n_ai) {
-                const int g = c * 32 + a_q[i] * 8;
-                const int aid = g / a.rp;
-                const uint16_t *p =
-                    a_ad[i] == aid ? a.S + (size_t)a_x[i] * a.rp + (g - aid * a.rp) : zeros;
-                load_lds16(p, sa + (wave + 4 * i) * 1024);
+        for (int t = 0; t < kNTW; ++t) {
+            const int nt16 = s64 * 4 + t;
+            b_col[t] = kGated ? (nt16 & 1) * a.I + (nt16 >> 1) * 16 + (lane & 15)
+                              : nt16 * 16 + (lane & 15);
+        }
+        const uint16_t *zeros = a.zeros;
+
+        // issue every load of chunk vc into stage st; `lean`: vc < KC
+        auto issue = [&](auto na, auto lean, int vc, int st) __attribute__((always_inline)) {
+            constexpr int NA = decltype(na)::value;
+            const uint32_t sa = smem_lds + (uint32_t)(st * kStageBytes);
+            const uint32_t sb = sa + kAStageBytes + g * kNTW * 1024;
+            if (decltype(lean)::value) {
+#pragma unroll
+                for (int i = 0; i < NA; ++i)
+                    load_lds16(a_src[i] + vc * 32, sa + (g + kCons * i) * 1024);
+#pragma unroll
+                for (int t = 0; t < kNTW; ++t) {
+                    if (has_cols)  // weights are read once: streaming hint
+                        load_lds16_stream(b_main + ((size_t)vc * 4 + t) * 512, sb + t * 1024);
+                    else
+                        load_lds16(zeros, sb + t * 1024);
+                }
+                return;
             }
-        }
-        const int g = c * 32 + (lane >> 4) * 8;
-        const int aid = g / a.rp;
-        const int q0 = g - aid * a.rp;
+            const int c = vc - KC;
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            const uint16_t *p =
-                aid < a.L ? a.LB + (((a.lb_shared ? (size_t)aid : (size_t)aid * a.E_l + le) *
-                                         a.n_canon + b_col[n]) * a.r + q0)
-                          : zeros;
-            load_lds16(p, sb + (2 * wave + n) * 1024);
+            for (int i = 0; i < NA; ++i) {
+                const int gq = c * 32 + a_q[i] * 8;
+                const int aid = gq / a.rp;
+                const uint16_t *p =
+                    a_ad[i] == aid ? a.S + (size_t)a_x[i] * a.rp + (gq - aid * a.rp) : zeros;
+                load_lds16(p, sa + (g + kCons * i) * 1024);
+            }
+            const int gq = c * 32 + (lane >> 4) * 8;
+            const int aid = gq / a.rp;
+            const int q0 = gq - aid * a.rp;
+#pragma unroll
+            for (int t = 0; t < kNTW; ++t) {
+                const uint16_t *p =
+                    (has_cols && aid < a.L)
+                        ? a.LB + (((a.lb_shared ? (size_t)aid : (size_t)aid * a.E_l + le) *
+                                       a.n_canon + b_col[t]) * a.r + q0)
+                        : zeros;
+                load_lds16(p, sb + t * 1024);
+            }
+        };
+        auto issue_any = [&](auto na, int vc, int st) __attribute__((always_inline)) {
+            if (vc < KC)
+                issue(na, std::true_type{}, vc, st);
+            else
+                issue(na, std::false_type{}, vc, st);
+        };
+        // The stage of chunk vc is vc % kStages.  Chunks vbeg .. vbeg + S - 2
+        // go out first; after the barrier of chunk vc, chunk vc + S - 1 goes
+        // into the stage chunk vc - 1 has left.  Past the last chunk the last
+        // one is issued again, so the loads per chunk never change: chunk vc
+        // has landed once only the (S - 2) chunks issued after it can be
+        // outstanding.
+        auto run = [&](auto na) __attribute__((always_inline)) {
+            constexpr int kLoads = decltype(na)::value + kNTW;
+            for (int d = 0; d < kStages - 1; ++d) {
+                const int vc = min(vbeg + d, vend - 1);
+                issue_any(na, vc, (vbeg + d) % kStages);
+            }
+            for (int vc = vbeg; vc < vend; ++vc) {
+                dma_wait_barrier<(kStages - 2) * kLoads>();
+                const int nvc = vc + kStages - 1;
+                if (nvc < KC)
+                    issue(na, std::true_type{}, nvc, nvc % kStages);
+                else
+                    issue_any(na, min(nvc, vend - 1), nvc % kStages);
+            }
+            dma_drain();  // no direct load may land after the block's LDS is released
+        };
+        switch (n_a) {
+        case 0: run(std::integral_constant<int, 0>{}); break;
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        default: run(std::integral_constant<int, 3>{}); break;
         }
-    };
+        return;
+    }
 
-    f32x4 acc[kWMT][2];
+    // -------------------------------------------------------------- consumer
+    f32x4 acc[kWMT][kNTW];
 #pragma unroll
     for (int m = 0; m < kWMT; ++m)
-        acc[m][0] = acc[m][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int t = 0; t < kNTW; ++t)
+            acc[m][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    lds_barrier();  // mt_adapters
     const int a_lane_off = (lane & 15) * 64 + (((lane >> 4) ^ a_swizzle(lane & 15)) * 16);
-    // M tiles that exist, as a scalar bit mask
-    const uint32_t main_tiles = __builtin_amdgcn_readfirstlane((1u << n_mt) - 1u);
+    // M tiles that exist (none for a column group past N), as a scalar mask
+    const uint32_t main_tiles =
+        __builtin_amdgcn_readfirstlane(has_cols ? (1u << n_mt) - 1u : 0u);
 
-    // multiply the chunk in stage st for the M tiles in `tiles`
-    auto compute = [&](int st, uint32_t tiles) {
-        const unsigned char *sa = stage(st);
-        const unsigned char *sb = sa + kAStageBytes + 2 * wave * 1024 + lane * 16;
-        const u32x4 b0 = *reinterpret_cast<const u32x4 *>(sb);
-        const u32x4 b1 = *reinterpret_cast<const u32x4 *>(sb + 1024);
-        // two halves of five M tiles: fragment reads, then their MFMAs (the
-        // scheduling barriers keep only one half's fragments live)
+    // multiply the chunk in stage st for the M tiles in `tiles`; A fragments
+    // are read two M tiles ahead of their MFMAs (a ring of three)
+    auto compute = [&](int st, uint32_t tiles) __attribute__((always_inline)) {
+        const unsigned char *sa = smem + st * kStageBytes;
+        const unsigned char *sb = sa + kAStageBytes + g * kNTW * 1024 + lane * 16;
+        u32x4 b[kNTW];
 #pragma unroll
-        for (int h = 0; h < kWMT; h += kWMT / 2) {
-            u32x4 av[kWMT / 2];
+        for (int t = 0; t < kNTW; ++t)
+            b[t] = *reinterpret_cast<const u32x4 *>(sb + t * 1024);
+        u32x4 av[3];
+        av[0] = *reinterpret_cast<const u32x4 *>(sa + a_lane_off);
+        av[1] = *reinterpret_cast<const u32x4 *>(sa + 1024 + a_lane_off);
 #pragma unroll
-            for (int m = 0; m < kWMT / 2; ++m)  // rows past the tile: read, never used
-                av[m] = *reinterpret_cast<const u32x4 *>(sa + (h + m) * 1024 + a_lane_off);
+        for (int m = 0; m < kWMT; ++m) {
+            if (m + 2 < kWMT)  // rows past the tile: read, never used
+                av[(m + 2) % 3] =
+                    *reinterpret_cast<const u32x4 *>(sa + (m + 2) * 1024 + a_lane_off);
+            if (tiles & (1u << m)) {
 #pragma unroll
-            for (int m = 0; m < kWMT / 2; ++m) {
-                if (tiles & (1u << (h + m))) {
-                    acc[h + m][0] = mfma_16x16x32(av[m], b0, acc[h + m][0]);
-                    acc[h + m][1] = mfma_16x16x32(av[m], b1, acc[h + m][1]);
-                }
+                for (int t = 0; t < kNTW; ++t)
+                    acc[m][t] = mfma_16x16x32(av[m % 3], b[t], acc[m][t]);
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
     };
     // M tiles holding a row of an adapter whose K block meets expand chunk vc
-    auto ext_tiles = [&](int vc) {
+    auto ext_tiles = [&](int vc) __attribute__((always_inline)) {
         const int lo = ((vc - KC) * 32) / a.rp;
         const int hi = min(a.L - 1, ((vc - KC) * 32 + 31) / a.rp);
         const int span = hi - lo + 1;
@@ -276,47 +327,16 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_wide_kernel(GemmArgs a)
             t |= (mt_adapters[m] & need) != 0 ? 1u << m : 0u;
         return __builtin_amdgcn_readfirstlane(t & main_tiles);
     };
-    // Per chunk a wave issues n_ai + 2 loads; chunk vc is complete once only
-    // the loads of the two chunks issued after it can be outstanding.
-    auto wait_chunk = [&]() {
-        if (n_ai == 3)
-            dma_wait_barrier<2 * (3 + 2)>();
-        else
-            dma_wait_barrier<2 * (2 + 2)>();
-    };
 
-    // The stage of chunk vc is vc % kStages.  Chunk vc + 3 is issued right
-    // after the barrier of chunk vc, into the stage chunk vc - 1 has left
-    // (every wave's reads of it are complete).  Past the last chunk the last
-    // one is issued again, so the loads per chunk never change.  Groups of
-    // four chunks whose loads are all main chunks take a lean path.
-    static_assert(kStages == 4, "the issue distance below is kStages - 1");
-    issue(vbeg, 0);
-    issue(min(vbeg + 1, vend - 1), 1);
-    issue(min(vbeg + 2, vend - 1), 2);
-    for (int vc0 = vbeg; vc0 < vend; vc0 += kStages) {
-        if (vc0 + kStages + 2 < KC) {
-#pragma unroll
-            for (int d = 0; d < kStages; ++d) {
-                wait_chunk();
-                issue_main(vc0 + d + 3, (d + 3) % kStages);
-                compute(d, main_tiles);
-            }
-        } else {
-#pragma unroll
-            for (int d = 0; d < kStages; ++d) {
-                const int vc = vc0 + d;
-                wait_chunk();
-                issue(min(vc + 3, vend - 1), (d + 3) % kStages);
-                if (vc < vend)
-                    compute(d, vc < KC ? main_tiles : ext_tiles(vc));
-            }
-        }
+    for (int vc = vbeg; vc < vend; ++vc) {
+        dma_wait_barrier<63>();  // chunk vc has landed; this wave's reads of vc - 1 are done
+        compute(vc % kStages, vc < KC ? main_tiles : ext_tiles(vc));
     }
-    dma_drain();  // no direct load may land after the block's LDS is released
 
     // epilogue straight from the accumulators: lane holds rows 4 (lane / 16) + i
-    // of each M tile, column lane % 16 of its two tiles
+    // of each M tile, column lane % 16 of its four tiles
+    if (!has_cols)
+        return;
     const int c = lane & 15;
 #pragma unroll
     for (int m = 0; m < kWMT; ++m) {
@@ -327,24 +347,28 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_wide_kernel(GemmArgs a)
                 if (r < n_rows) {
                     const size_t p = (size_t)(row0 + r);
                     if (kGated) {
-                        const int j = slab * 4 + wave;  // gate/up pair of this wave
-                        const size_t h_at = p * 2 * a.I + j * 16 + c;
-                        float gate = acc[m][0][i], up = acc[m][1][i];
-                        if (a.phase == 1) {  // fp32 pre-activation for phase 2
-                            a.H[h_at] = gate;
-                            a.H[h_at + a.I] = up;
-                        } else {
-                            if (a.phase == 2) {
-                                gate += a.H[h_at];
-                                up += a.H[h_at + a.I];
+#pragma unroll
+                        for (int q = 0; q < kNTW / 2; ++q) {
+                            const int j = 2 * s64 + q;  // gate/up pair: tiles 2 j, 2 j + 1
+                            const size_t h_at = p * 2 * a.I + j * 16 + c;
+                            float gate = acc[m][2 * q][i], up = acc[m][2 * q + 1][i];
+                            if (a.phase == 1) {  // fp32 pre-activation for phase 2
+                                a.H[h_at] = gate;
+                                a.H[h_at + a.I] = up;
+                            } else {
+                                if (a.phase == 2) {
+                                    gate += a.H[h_at];
+                                    up += a.H[h_at + a.I];
+                                }
+                                a.Y[p * a.I + j * 16 + c] =
+                                    (uint16_t)float_to_bf16_bits(silu_f32(gate) * up);
                             }
-                            a.Y[p * a.I + j * 16 + c] =
-                                (uint16_t)float_to_bf16_bits(silu_f32(gate) * up);
                         }
                     } else {
-                        const int col = slab * 128 + wave * 32 + c;
-                        a.Y[p * a.n_canon + col] = (uint16_t)float_to_bf16_bits(acc[m][0][i]);
-                        a.Y[p * a.n_canon + col + 16] = (uint16_t)float_to_bf16_bits(acc[m][1][i]);
+#pragma unroll
+                        for (int t = 0; t < kNTW; ++t)
+                            a.Y[p * a.n_canon + s64 * 64 + t * 16 + c] =
+                                (uint16_t)float_to_bf16_bits(acc[m][t][i]);
                     }
                 }
             }
@@ -359,15 +383,17 @@ bool gemm_wide_supported(int H, int I, int r_gu, int r_dn)
     return I % 64 == 0 && H % 128 == 0 && r_gu % 8 == 0 && r_dn % 8 == 0;
 }
 
+int gemm_wide_slabs(int NT) { return (NT * 16 + kSlabCols - 1) / kSlabCols; }
+
 hipError_t launch_gemm_wide(const GemmArgs &a, bool gated, hipStream_t s)
 {
     const int blocks = gemm_grid_blocks(a.n_tiles, a.n_slabs);
     if (blocks <= 0)
         return hipSuccess;
     if (gated)
-        hipLaunchKernelGGL((expert_gemm_wide_kernel<true>), dim3(blocks), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((expert_gemm_wide_kernel<true>), dim3(blocks), dim3(kThreadsW), 0, s, a);
     else
-        hipLaunchKernelGGL((expert_gemm_wide_kernel<false>), dim3(blocks), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((expert_gemm_wide_kernel<false>), dim3(blocks), dim3(kThreadsW), 0, s, a);
     return hipGetLastError();
 }
 

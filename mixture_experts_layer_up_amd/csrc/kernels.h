@@ -123,12 +123,14 @@ struct GemmArgs {
 };
 
 // Rows per GEMM work-list tile: 16 for the decode-shaped kernel (few rows
-// per expert), 160 for the wide kernel (many rows per expert, when the
-// shape allows it).
+// per expert); for the wide kernel (many rows per expert, when the shape
+// allows it) a multiple of 16 up to kWideMaxTileRows, chosen so that one
+// tile usually holds all rows of an expert.
 constexpr int kDecodeTileRows = 16;
-constexpr int kWideTileRows = 160;
+constexpr int kWideMaxTileRows = 176;
 // r_gu, r_dn: ranks of the active LoRA projections (0 when inactive)
 bool gemm_wide_supported(int H, int I, int r_gu, int r_dn);
+int gemm_wide_slabs(int NT);  // column slabs of the wide kernel for NT 16-column tiles
 int gemm_tile_rows(int n_slots, int E_l, int H, int I, int r_gu, int r_dn);
 hipError_t launch_gemm_wide(const GemmArgs &a, bool gated, hipStream_t s);
 

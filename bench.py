@@ -140,6 +140,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 GEMM_SOURCES = ["mixture_experts_layer_up_amd/csrc/expert_gemm.hip",
                 "mixture_experts_layer_up_amd/csrc/expert_gemm_wide.hip",
                 "mixture_experts_layer_up_amd/csrc/device_common.h",
+                "mixture_experts_layer_up_amd/csrc/lds_dma.h",
                 "mixture_experts_layer_up_amd/csrc/kernels.h"]
 DOMINANT = {"decode": "expert_gemm_kernel<1, 1, true, true>", "prefill": "expert_gemm_wide_kernel<true>"}
 

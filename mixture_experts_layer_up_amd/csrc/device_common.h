@@ -117,7 +117,13 @@ __device__ __forceinline__ int xcd_balanced_item(int bid, int n_items)
     return item < n_items ? item : -1;
 }
 
+// SiLU(z) = z * sigmoid(z) from the hardware base-2 exponential and
+// reciprocal (v_exp_f32, v_rcp_f32; each within about one fp32 ulp): the
+// epilogues round the gated product to bf16, far coarser, and a library
+// exp plus an IEEE division per element cost several microseconds per
+// many-row GEMM block.  z -> -inf gives -0, z -> +inf gives z.
 __device__ __forceinline__ float silu_f32(float z)
 {
-    return z / (1.0f + expf(-z));
+    const float e = __builtin_amdgcn_exp2f(-z * 1.44269504088896340736f);  // exp(-z)
+    return z * __builtin_amdgcn_rcpf(1.0f + e);
 }

@@ -512,6 +512,9 @@ hipError_t launch_shrink(const ShrinkArgs &a, hipStream_t s)
     // rows per pass from the mean rows per (adapter, expert) segment when
     // every slot carries an adapter: one pass covers most segments
     const int mean = (a.n_slots + blocks - 1) / blocks;
+    // segments of tens of rows: the direct-load kernel (lora_shrink_wide.hip)
+    if (mean >= 16 && shrink_wide_supported(a.r))
+        return launch_shrink_wide(a, mean, s);
     const int mt = mean <= 8 ? 1 : mean <= 24 ? 2 : 3;
     if (a.r <= 16) {
         if (mt == 1)

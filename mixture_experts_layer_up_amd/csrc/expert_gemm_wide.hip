@@ -35,6 +35,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace moe_lora {
 namespace {
@@ -51,68 +52,18 @@ constexpr int kBStageBytes = kCons * kNTW * 1024;  // 16 MFMA B fragments
 constexpr int kStageBytes = kAStageBytes + kBStageBytes;
 constexpr int kAPerProd = (kWMT + kCons - 1) / kCons;  // A loads per producer: 3
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16-byte direct load into LDS: lane l's 16 bytes land at LDS byte address
-// lds_addr + 16 l (lds_addr wave-uniform).  Written as inline assembly on
-// purpose: the compiler then leaves the completion of these loads entirely
-// to the explicit waits below (its own tracking would otherwise wait for
-// every outstanding load before each LDS read and serialise the pipeline).
-// Loads it does not know about can only make its own wait counts stricter.
-__device__ __forceinline__ void load_lds16(const void *g, uint32_t lds_addr)
-{
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :
-                 : "s"(lds_addr), "v"(g)
-                 : "memory", "m0");
-}
-
-// The same for data read once (expert weights): the nontemporal hint keeps
-// the weight stream from evicting the activation rows that the other column
-// slabs of the expert are about to read from L2.
-__device__ __forceinline__ void load_lds16_stream(const void *g, uint32_t lds_addr)
-{
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt"
-                 :
-                 : "s"(lds_addr), "v"(g)
-                 : "memory", "m0");
-}
-
-// Physical 16-byte quarter of logical quarter q of activation row `row`.
-__device__ __forceinline__ int a_swizzle(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
-
-// Wait until at most N of this wave's vector loads are outstanding and its
-// LDS reads are done, then synchronise the block (N = 63: LDS reads only).
-// The direct loads write LDS behind the compiler's back, so this wait is
-// spelled out; the empty asm statements keep LDS reads from moving across
-// the barrier.
-template <int N>
-__device__ __forceinline__ void dma_wait_barrier()
-{
-    static_assert(N < 64, "vmcnt field is 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));  // lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ void dma_drain()
-{
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
-    asm volatile("" ::: "memory");
-}
-
 template <bool kGated>
 __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs a)
 {
     __shared__ __align__(1024) unsigned char smem[kStages * kStageBytes];
     // LDS byte address of smem, for the direct loads (M0)
-    const uint32_t smem_lds =
-        __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_void *)smem));
+    const uint32_t smem_lds = lds_address(smem);
     __shared__ int row_x[kWRows];
     __shared__ int row_src[kWRows];
     __shared__ int row_adapter[kWRows];
     __shared__ unsigned long long mt_adapters[kWMT];
+    // each consumer's output staging tile: 16 rows x up to 64 bf16 columns
+    __shared__ __align__(16) uint16_t otile[kCons][16 * kNTW * 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -182,7 +133,7 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
         for (int i = 0; i < kAPerProd; ++i) {
             const int j = min(g + kCons * i, kWMT - 1);
             const int pr = 16 * j + (lane >> 2);
-            const int q = (lane & 3) ^ a_swizzle(pr);
+            const int q = (lane & 3) ^ act_swizzle(pr);
             a_src[i] = a.X + (size_t)row_src[pr] * a.K + q * 8;
             a_x[i] = row_x[pr];
             a_ad[i] = row_adapter[pr];
@@ -286,7 +237,7 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
         for (int t = 0; t < kNTW; ++t)
             acc[m][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int a_lane_off = (lane & 15) * 64 + (((lane >> 4) ^ a_swizzle(lane & 15)) * 16);
+    const int a_lane_off = (lane & 15) * 64 + (((lane >> 4) ^ act_swizzle(lane & 15)) * 16);
     // M tiles that exist (none for a column group past N), as a scalar mask
     const uint32_t main_tiles =
         __builtin_amdgcn_readfirstlane(has_cols ? (1u << n_mt) - 1u : 0u);
@@ -333,45 +284,76 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
         compute(vc % kStages, vc < KC ? main_tiles : ext_tiles(vc));
     }
 
-    // epilogue straight from the accumulators: lane holds rows 4 (lane / 16) + i
-    // of each M tile, column lane % 16 of its four tiles
+    // Epilogue.  Lane holds rows 4 (lane / 16) + i of each M tile, column
+    // lane % 16 of its four tiles.  Phase 1 writes the fp32 pre-activation
+    // element by element; otherwise each M tile's bf16 outputs (SwiGLU'd for
+    // gate_up) go through this consumer's private LDS tile, 16 rows x kOut
+    // columns, and leave as 16-byte row segments.
     if (!has_cols)
         return;
     const int c = lane & 15;
+    if (kGated && a.phase == 1) {
+#pragma unroll
+        for (int m = 0; m < kWMT; ++m) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = m * 16 + 4 * (lane >> 4) + i;
+                if (m < n_mt && r < n_rows) {
+                    const size_t p = (size_t)(row0 + r);
+#pragma unroll
+                    for (int q = 0; q < kNTW / 2; ++q) {
+                        const size_t h_at = p * 2 * a.I + (2 * s64 + q) * 16 + c;
+                        a.H[h_at] = acc[m][2 * q][i];
+                        a.H[h_at + a.I] = acc[m][2 * q + 1][i];
+                    }
+                }
+            }
+        }
+        return;
+    }
+    constexpr int kOut = kGated ? kNTW / 2 * 16 : kNTW * 16;  // output columns: 32 or 64
+    constexpr int kSeg = kOut / 8;                            // 16-byte segments per row
+    uint16_t *ot = otile[g];
+    // this consumer's output columns start at column `col0` of the output rows
+    const int col0 = kGated ? 2 * s64 * 16 : s64 * 64;
+    const int ld = kGated ? a.I : a.n_canon;
 #pragma unroll
     for (int m = 0; m < kWMT; ++m) {
         if (m < n_mt) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = m * 16 + 4 * (lane >> 4) + i;
-                if (r < n_rows) {
-                    const size_t p = (size_t)(row0 + r);
-                    if (kGated) {
+                const int rr = 4 * (lane >> 4) + i;
+                if (kGated) {
 #pragma unroll
-                        for (int q = 0; q < kNTW / 2; ++q) {
-                            const int j = 2 * s64 + q;  // gate/up pair: tiles 2 j, 2 j + 1
-                            const size_t h_at = p * 2 * a.I + j * 16 + c;
-                            float gate = acc[m][2 * q][i], up = acc[m][2 * q + 1][i];
-                            if (a.phase == 1) {  // fp32 pre-activation for phase 2
-                                a.H[h_at] = gate;
-                                a.H[h_at + a.I] = up;
-                            } else {
-                                if (a.phase == 2) {
-                                    gate += a.H[h_at];
-                                    up += a.H[h_at + a.I];
-                                }
-                                a.Y[p * a.I + j * 16 + c] =
-                                    (uint16_t)float_to_bf16_bits(silu_f32(gate) * up);
-                            }
+                    for (int q = 0; q < kNTW / 2; ++q) {
+                        float gate = acc[m][2 * q][i], up = acc[m][2 * q + 1][i];
+                        if (a.phase == 2 && m * 16 + rr < n_rows) {
+                            const size_t h_at =
+                                (size_t)(row0 + m * 16 + rr) * 2 * a.I + (2 * s64 + q) * 16 + c;
+                            gate += a.H[h_at];
+                            up += a.H[h_at + a.I];
                         }
-                    } else {
-#pragma unroll
-                        for (int t = 0; t < kNTW; ++t)
-                            a.Y[p * a.n_canon + s64 * 64 + t * 16 + c] =
-                                (uint16_t)float_to_bf16_bits(acc[m][t][i]);
+                        ot[rr * kOut + q * 16 + c] =
+                            (uint16_t)float_to_bf16_bits(silu_f32(gate) * up);
                     }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < kNTW; ++t)
+                        ot[rr * kOut + t * 16 + c] = (uint16_t)float_to_bf16_bits(acc[m][t][i]);
                 }
             }
+            // one wave: its LDS operations complete in order, so the reads
+            // below see every lane's writes above
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int h = 0; h < 16 * kSeg / kWave; ++h) {
+                const int e = h * kWave + lane;  // 16-byte segment: row e / kSeg
+                const int rr = e / kSeg, sg = e % kSeg;
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(ot + rr * kOut + sg * 8);
+                if (m * 16 + rr < n_rows)
+                    store16(a.Y + (size_t)(row0 + m * 16 + rr) * ld + col0 + sg * 8, v);
+            }
+            __builtin_amdgcn_wave_barrier();
         }
     }
 }

@@ -147,6 +147,9 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t s);
 hipError_t launch_permute(const PermuteArgs &a, hipStream_t s);
 hipError_t launch_pack(const PackArgs &a, hipStream_t s);
 hipError_t launch_shrink(const ShrinkArgs &a, hipStream_t s);
+// the shrink for segments of many rows: rank r <= 64, mean_rows per segment
+bool shrink_wide_supported(int r);
+hipError_t launch_shrink_wide(const ShrinkArgs &a, int mean_rows, hipStream_t s);
 hipError_t launch_gemm_gate_up(const GemmArgs &a, hipStream_t s);
 hipError_t launch_gemm_down(const GemmArgs &a, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs &a, hipStream_t s);

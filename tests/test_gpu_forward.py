@@ -29,8 +29,9 @@ MID_EP = MID.replace(name="mid_ep", local_expert_offset=5, local_num_experts=7, 
 BIG_ROWS = LayerConfig("big_rows", 300, 128, 64, 4, 1, 0, 4, 2, 16, 16, seed=34,
                        mapping="uniform", sigma_lora_a=0.2, sigma_lora_b=0.2)
 TINY_AMP = CONFIGS["tiny"].replace(name="tiny_amp", sigma_lora_a=0.2, sigma_lora_b=0.2)
-# Many rows per expert (the 160-row tile kernel): ~350 rows per expert, so
-# three row tiles with a ragged last one; 3 adapters of rank 24, so a K chunk
+# Many rows per expert (the many-row GEMM and shrink kernels): ~350 rows per
+# expert, so two 176-row tiles with a ragged last one, and ~117-row LoRA
+# segments, so two shrink passes of 64 rows; 3 adapters of rank 24, so a K chunk
 # of the LoRA expand spans two adapters and the last chunk is partial; tokens
 # without adapter leave some 16-row tiles out of the expand.
 WIDE = LayerConfig("wide", 700, 256, 192, 4, 2, 0, 4, 3, 24, 24, seed=35, mapping="uniform",
@@ -42,6 +43,10 @@ WIDE_H128 = WIDE.replace(name="wide_h128", hidden=128)
 WIDE_R8 = WIDE.replace(name="wide_r8", num_tokens=520, num_loras=1, rank_gate_up=8,
                        rank_down=8, mapping="runs", run_length=130, seed=36,
                        sigma_lora_a=0.2, sigma_lora_b=0.2)
+# ~37 rows per LoRA segment (the many-row shrink) with ranks that are not
+# multiples of 8 (zero-padded shrink rows; the 16-row GEMM tiles)
+SHRINK_R20 = LayerConfig("shrink_r20", 300, 256, 96, 8, 2, 0, 8, 2, 20, 12, seed=37,
+                         mapping="uniform", sigma_lora_a=0.2, sigma_lora_b=0.2)
 
 
 def _compare(cfg, inp, got, tokens=None, **kw):
@@ -77,7 +82,7 @@ def test_prefill_sampled_tokens():
 
 
 @pytest.mark.parametrize("cfg", [MID, MID_R64, MID_EP, BIG_ROWS, TINY_AMP, WIDE, WIDE_R8,
-                                 WIDE_H128],
+                                 WIDE_H128, SHRINK_R20],
                          ids=lambda c: c.name)
 def test_small_shapes_and_lora_delta(cfg):
     announce(f"forward {cfg.name}")

@@ -14,7 +14,7 @@ import pytest
 
 from mixture_experts_layer_up_amd import build
 
-SOURCES = [f for f in build.sources() if "expert_gemm" in f]
+SOURCES = [f for f in build.sources() if "expert_gemm" in f or "lora_shrink" in f]
 
 
 def _device_asm(src, tmp_path):

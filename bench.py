@@ -32,10 +32,10 @@ WORKLOAD_TEXT = {
     "decode64": "multi-adapter decode: T=64 tokens, hidden 2048, 128 experts top-8, inter 768 "
                 "SwiGLU, 4 LoRA adapters rank 16 on gate_up and down, mapping uniform over "
                 "{-1,0,1,2,3}, 4 hot experts",
-    "decode16": "decode: T=16, hidden 2048, 128 experts top-8, inter 768, 1 adapter rank 16",
+    "decode16": "T=16, hidden 2048, 128 experts top-8, inter 768, 1 adapter rank 16",
     "ep_shard": "expert-parallel shard: T=64, hidden 2048, 32 of 128 experts local (offset 32), "
                 "top-8, inter 768, 4 adapters rank 16",
-    "prefill": "prefill: T=2048, hidden 2048, 128 experts top-8, inter 768, 4 adapters rank 64 "
+    "prefill": "T=2048, hidden 2048, 128 experts top-8, inter 768, 4 adapters rank 64 "
                "in runs of 512 tokens",
     "tiny": "tiny: T=8, hidden 128, 8 experts top-2, inter 64, 2 adapters rank 4",
 }

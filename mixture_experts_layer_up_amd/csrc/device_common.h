@@ -15,14 +15,12 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16)
     return __uint_as_float(bits16 << 16);
 }
 
-// Round to nearest even; NaN stays NaN.
+// Round to nearest even; NaN stays NaN.  gfx950 converts in hardware
+// (v_cvt_pk_bf16_f32), one instruction instead of the integer rounding
+// sequence.
 __device__ __forceinline__ uint32_t float_to_bf16_bits(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ u32x4 load16(const void *p)

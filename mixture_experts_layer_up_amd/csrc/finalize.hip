@@ -25,17 +25,33 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a)
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         acc[i] = 0.0f;
-    for (int j = 0; j < a.k; ++j) {
-        const int p = a.exp2perm[(size_t)t * a.k + j];
-        if (p < 0)
-            continue;
-        const float w = a.weights[(size_t)t * a.k + j];
-        const u32x4 v = load16(a.Y + (size_t)p * a.H + col0);
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    // slots in groups of 8: every index and row load of a group is issued
+    // before any is used (the rows depend on the indices, so a plain loop
+    // would wait twice per slot); the sum still runs in ascending j
+    constexpr int kG = 8;
+    for (int j0 = 0; j0 < a.k; j0 += kG) {
+        int p[kG];
+        float w[kG];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[2 * i] += w * bf16_bits_to_float(u[i] & 0xffffu);
-            acc[2 * i + 1] += w * bf16_bits_to_float(u[i] >> 16);
+        for (int i = 0; i < kG; ++i) {
+            const int j = min(j0 + i, a.k - 1);
+            p[i] = j0 + i < a.k ? a.exp2perm[(size_t)t * a.k + j] : -1;
+            w[i] = a.weights[(size_t)t * a.k + j];
+        }
+        u32x4 v[kG];
+#pragma unroll
+        for (int i = 0; i < kG; ++i)  // slots that are not local read row 0, unused
+            v[i] = load16(a.Y + (size_t)max(p[i], 0) * a.H + col0);
+#pragma unroll
+        for (int i = 0; i < kG; ++i) {
+            const uint32_t u[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float lo = acc[2 * e] + w[i] * bf16_bits_to_float(u[e] & 0xffffu);
+                const float hi = acc[2 * e + 1] + w[i] * bf16_bits_to_float(u[e] >> 16);
+                acc[2 * e] = p[i] >= 0 ? lo : acc[2 * e];
+                acc[2 * e + 1] = p[i] >= 0 ? hi : acc[2 * e + 1];
+            }
         }
     }
     u32x4 o;

@@ -273,6 +273,8 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain copy kernel (torch.neg) over this many MiB, "
                          "to calibrate HBM byte counters against a known size")
+    ap.add_argument("--cold-steps", type=int, default=30,
+                    help="steps timed one by one after a 512 MiB cache flush (0 = skip)")
     ap.add_argument("--graph", type=int, default=1,
                     help="also time the K steps as one HIP-graph replay (1 = yes)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "OUT_MD"),
@@ -425,6 +427,30 @@ def main():
         del g
         log(f"[bench] graph replay: {graph_ms * 1e3:.1f} us/step")
 
+    # Cold cache (diagnostic, outside the timed region): before each of KC
+    # steps a 512 MiB buffer is rewritten, so the 256 MiB Infinity Cache
+    # holds none of the layer's data; each step is timed alone between two
+    # events.  Back-to-back steps (the timed region) keep only what the
+    # previous step left in that cache.
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cev = [hip.create(2) for _ in range(args.cold_steps)]
+        for s_, (a_, b_) in enumerate(cev):
+            flush.fill_(s_ & 0xff)
+            hip.record(a_, stream)
+            step()
+            hip.record(b_, stream)
+        torch.cuda.synchronize()
+        cms = np.array([hip.elapsed_ms(a_, b_) for a_, b_ in cev])
+        for e in cev:
+            hip.destroy(e)
+        del flush
+        cold = {"steps": args.cold_steps, "ms_median": float(np.median(cms)),
+                "ms_p90": float(np.percentile(cms, 90)), "ms_min": float(cms.min()),
+                "tokens_per_s_median": cfg.num_tokens / (float(np.median(cms)) / 1e3)}
+        log(f"[bench] cold cache: median {cold['ms_median'] * 1e3:.1f} us/step")
+
     # the cost model counts what this batch's routing touches (the library's own routing)
     routing = binding.alloc_routing(shape, "cuda")
     binding.forward(shape, lay["hidden"], lay["w13_packed"], lay["w2_packed"], out=out,
@@ -484,6 +510,8 @@ def main():
         "graph_replay": None if graph_ms is None else {
             "ms_per_step": graph_ms, "tokens_per_s": cfg.num_tokens / (graph_ms / 1e3),
             "layer_hbm_frac": cost["bytes"] / (graph_ms / 1e3) / 1e9 / HBM_PEAK_GBPS},
+        "cold_cache": None if cold is None else {
+            **cold, "layer_hbm_frac": cost["bytes"] / (cold["ms_median"] / 1e3) / 1e9 / HBM_PEAK_GBPS},
         "cpu_baseline": cpu,
     }
     print(json.dumps(result))

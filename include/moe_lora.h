@@ -126,7 +126,19 @@ typedef struct moe_lora_routing {
     int32_t *permuted_idx_to_expanded_idx;
     int32_t *lora_seg_offsets;
     int32_t *lora_seg_slots;
+    int32_t *input_flags;   /* optional, see MOE_LORA_FLAG_* (moe_lora_route) */
 } moe_lora_routing;
+
+/*
+ * Bad device-side values never fault: an expert id of a given top-k outside
+ * [-1, num_experts) is a slot of no local expert (as -1 is), a
+ * token_lora_mapping value outside [-1, num_loras) is -1.  When the caller
+ * passes an `input_flags` pointer (one device int32, caller-owned), the call
+ * ORs these bits into it for what it met; it never clears them, so the caller
+ * zeroes the word and reads it after the stream has passed the call.
+ */
+#define MOE_LORA_FLAG_EXPERT_ID 1  /* a top-k id outside [-1, num_experts) */
+#define MOE_LORA_FLAG_ADAPTER   2  /* a token_lora_mapping value outside [-1, num_loras) */
 
 /*
  * Forward inputs.  Exactly one of `router_logits` or the pair
@@ -180,6 +192,9 @@ typedef struct moe_lora_routing {
  *                      GEMM is then split in two launches joined by an fp32
  *                      pre-activation in the workspace: results equal the
  *                      one-stream ones within rounding, not bitwise.
+ *   input_flags        NULL, or one device int32 into which the MOE_LORA_FLAG_*
+ *                      bits of this call are ORed (when NULL and `routing`
+ *                      is given, routing->input_flags is used)
  *   fork_event,        caller-owned hipEvent_t handles (timing may be
  *   join_event         disabled), required with side_stream: fork_event is
  *                      recorded on `stream` after routing and waited by
@@ -208,6 +223,7 @@ typedef struct moe_lora_inputs {
     void *side_stream;
     void *fork_event;
     void *join_event;
+    int32_t *input_flags;
 } moe_lora_inputs;
 
 /* Bytes of device workspace moe_lora_forward needs for `shape` (host only,
@@ -243,7 +259,8 @@ int moe_lora_pack_weights(const moe_lora_shape *shape, const void *w13, const vo
  * optional `routing_bias`, as in moe_lora_inputs) when given, else takes
  * `topk_ids` / `topk_weights` as they are (then routing->topk_ids
  * and routing->topk_weights are not written and may be NULL).  Every other
- * field of `routing` must be non-NULL.  `token_lora_mapping` as in
+ * field of `routing` must be non-NULL, except `input_flags` (optional: the
+ * MOE_LORA_FLAG_* bits of this call are ORed into it).  `token_lora_mapping` as in
  * moe_lora_inputs.  `workspace` is device memory of at least
  * moe_lora_route_workspace_size(shape) bytes, 16-byte aligned (the permute's
  * per-block histograms; its contents on entry do not matter); it may be NULL

@@ -44,7 +44,7 @@ class Routing(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in (
         "topk_ids", "topk_weights", "expert_counts", "expert_offsets",
         "expanded_idx_to_permuted_idx", "permuted_idx_to_expanded_idx",
-        "lora_seg_offsets", "lora_seg_slots")]
+        "lora_seg_offsets", "lora_seg_slots", "input_flags")]
 
 
 class Inputs(ctypes.Structure):
@@ -53,10 +53,12 @@ class Inputs(ctypes.Structure):
         "w2_packed",
         "lora_a_gate_up", "lora_b_gate_up", "lora_a_down", "lora_b_down",
         "token_lora_mapping", "stage_events", "expert_out", "side_stream", "fork_event",
-        "join_event")]
+        "join_event", "input_flags")]
 
 
 NUM_STAGE_EVENTS = 7
+FLAG_EXPERT_ID = 1   # a given top-k id outside [-1, num_experts)
+FLAG_ADAPTER = 2     # a token_lora_mapping value outside [-1, num_loras)
 STAGE_NAMES = ("route_permute", "lora_shrink_gate_up", "gemm_gate_up_swiglu",
                "lora_shrink_down", "gemm_down", "finalize")
 
@@ -183,11 +185,16 @@ def route(shape: Shape, router_logits: Optional[torch.Tensor] = None,
           token_lora_mapping: Optional[torch.Tensor] = None,
           routing: Optional[Dict[str, torch.Tensor]] = None,
           routing_bias: Optional[torch.Tensor] = None,
-          workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+          workspace: Optional[torch.Tensor] = None,
+          input_flags: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Routing and permutation only.  ``input_flags`` (int32, one element)
+    receives the MOE_LORA_FLAG_* bits of bad ids / adapters met (ORed in)."""
     T, E, k = shape.num_tokens, shape.num_experts, shape.top_k
     dev = (router_logits if router_logits is not None else topk_ids).device
     r = routing if routing is not None else alloc_routing(shape, dev)
     rs = _routing_struct(r)
+    if input_flags is not None:
+        rs.input_flags = _ptr(input_flags, torch.int32, (1,), "input_flags")
     need = int(load_library().moe_lora_route_workspace_size(ctypes.byref(shape)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -213,14 +220,16 @@ def forward(shape: Shape, hidden: torch.Tensor, w13_packed: torch.Tensor,
             stage_events: Optional[Sequence[int]] = None,
             expert_out: Optional[torch.Tensor] = None,
             side_stream: Optional[int] = None, fork_event: Optional[int] = None,
-            join_event: Optional[int] = None) -> Optional[torch.Tensor]:
+            join_event: Optional[int] = None,
+            input_flags: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
     """One layer forward on the current stream; returns ``out`` bf16 [T, H].
 
     With ``expert_out`` (bf16 [T*k, H]) the per-slot expert outputs are
     written there at their permuted rows and the finalize is skipped (returns
     None; needs ``routing``); :func:`finalize` completes it.  ``side_stream``,
     ``fork_event``, ``join_event`` (raw hipStream_t / hipEvent_t handles)
-    select the two-stream schedule for the gate_up LoRA.
+    select the two-stream schedule for the gate_up LoRA.  ``input_flags``
+    (int32, one element) receives the MOE_LORA_FLAG_* bits (ORed in).
     """
     T, H, I, E, k = shape.num_tokens, shape.hidden, shape.inter, shape.num_experts, shape.top_k
     E_l, L, rg, rd = shape.local_num_experts, shape.num_loras, shape.rank_gate_up, shape.rank_down
@@ -253,6 +262,7 @@ def forward(shape: Shape, hidden: torch.Tensor, w13_packed: torch.Tensor,
         ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None,
         _ptr(expert_out, _BF16, (T * k, H), "expert_out"),
         side_stream, fork_event, join_event,
+        _ptr(input_flags, torch.int32, (1,), "input_flags"),
     )
     rs = _routing_struct(routing) if routing is not None else None
     _check(load_library().moe_lora_forward(

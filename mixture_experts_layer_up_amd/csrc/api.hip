@@ -126,8 +126,8 @@ struct RoutingPtrs {
 
 // block_counts: permute_scratch_bytes of workspace (unused for one slot block)
 int enqueue_routing(const moe_lora_shape *s, const float *logits, const float *bias,
-                    const int32_t *topk_ids, const int32_t *mapping, const RoutingPtrs &r,
-                    int32_t *block_counts, hipStream_t st,
+                    const int32_t *topk_ids, const int32_t *mapping, int32_t *flags,
+                    const RoutingPtrs &r, int32_t *block_counts, hipStream_t st,
                     int4 *tiles = nullptr, int tile_rows = 0, int max_tiles = 0,
                     int32_t *tile_count = nullptr, void *zeros = nullptr)
 {
@@ -157,6 +157,8 @@ int enqueue_routing(const moe_lora_shape *s, const float *logits, const float *b
     pa.zeros = static_cast<u32x4_t *>(zeros);
     pa.G = permute_blocks(s->num_tokens * s->top_k);
     pa.block_counts = block_counts;
+    pa.E = s->num_experts;
+    pa.flags = flags;
     return check(launch_permute(pa, st));
 }
 
@@ -270,8 +272,9 @@ int moe_lora_route(const moe_lora_shape *shape, const float *router_logits,
                   routing->expert_offsets, routing->expanded_idx_to_permuted_idx,
                   routing->permuted_idx_to_expanded_idx, routing->lora_seg_offsets,
                   routing->lora_seg_slots};
-    return enqueue_routing(shape, router_logits, routing_bias, topk_ids, token_lora_mapping, r,
-                           static_cast<int32_t *>(workspace), static_cast<hipStream_t>(stream));
+    return enqueue_routing(shape, router_logits, routing_bias, topk_ids, token_lora_mapping,
+                           routing->input_flags, r, static_cast<int32_t *>(workspace),
+                           static_cast<hipStream_t>(stream));
 }
 
 int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
@@ -366,8 +369,9 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     int4 *tiles = reinterpret_cast<int4 *>(ws + lay.tiles);
     void *zeros = ws + lay.zeros;
     int32_t *tile_count = reinterpret_cast<int32_t *>(ws + lay.tile_count);
+    int32_t *flags = in->input_flags ? in->input_flags : routing ? routing->input_flags : nullptr;
     MOE_TRY(enqueue_routing(shape, in->router_logits, in->routing_bias, in->topk_ids,
-                            in->token_lora_mapping, r,
+                            in->token_lora_mapping, flags, r,
                             reinterpret_cast<int32_t *>(ws + lay.perm_scratch), st,
                             tiles, lay.tile_rows, lay.max_tiles, tile_count, zeros));
     MOE_TRY(record(ev, 1, st));

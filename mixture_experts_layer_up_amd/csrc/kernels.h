@@ -34,6 +34,8 @@ struct PermuteArgs {
     u32x4_t *zeros;            // kZeroBytes written as zero (for the GEMMs)
     int G;                     // slot blocks: permute_blocks(T * k)
     int32_t *block_counts;     // G > 1: permute_scratch_bytes of workspace
+    int E;                     // global experts: valid ids are [-1, E)
+    int32_t *flags;            // MOE_LORA_FLAG_* bits ORed in (or null)
 };
 
 // The permute cuts the slots into blocks of kPermuteSlotsPerBlock; with more

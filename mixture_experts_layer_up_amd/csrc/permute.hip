@@ -25,6 +25,7 @@
 // histogram is the whole one and the count kernel is skipped.
 #include "device_common.h"
 #include "kernels.h"
+#include "moe_lora.h"
 
 namespace moe_lora {
 namespace {
@@ -71,9 +72,11 @@ __device__ __forceinline__ BlockSlots block_slots(int n, int g)
 // The keys of this lane's slots: group i holds slot beg + wave * chunk +
 // 64 i + lane (-1 past the block or the wave's chunk).  All loads are issued
 // before any is used.
+// key[i] of this lane's slots; bad: MOE_LORA_FLAG_* bits of the values read
+// (expert blocks check the ids, segment blocks the adapters)
 __device__ __forceinline__ void load_keys(const PermuteArgs &a, bool by_segment,
                                           const BlockSlots &b, int wave, int lane,
-                                          int (&key)[kIters])
+                                          int (&key)[kIters], int &bad)
 {
     int id[kIters], l[kIters];
 #pragma unroll
@@ -89,10 +92,16 @@ __device__ __forceinline__ void load_keys(const PermuteArgs &a, bool by_segment,
                 l[i] = a.mapping[x / a.k];
         }
     }
+    bad = 0;
 #pragma unroll
     for (int i = 0; i < kIters; ++i) {
         const int x = b.beg + wave * b.chunk + i * kWave + lane;
-        key[i] = (i < b.groups && x < b.end) ? key_from(a, by_segment, id[i], l[i]) : -1;
+        const bool slot = i < b.groups && x < b.end;
+        key[i] = slot ? key_from(a, by_segment, id[i], l[i]) : -1;
+        if (slot && !by_segment && (id[i] < -1 || id[i] >= a.E))
+            bad |= MOE_LORA_FLAG_EXPERT_ID;
+        if (slot && by_segment && (l[i] < -1 || l[i] >= a.L))
+            bad |= MOE_LORA_FLAG_ADAPTER;
     }
 }
 
@@ -135,7 +144,8 @@ __global__ __launch_bounds__(kThreads) void permute_count_kernel(PermuteArgs a)
     const int n = a.T * a.k;
     const BlockSlots b = block_slots(n, g);
     int key[kIters];
-    load_keys(a, by_segment, b, wave, lane, key);
+    int bad;
+    load_keys(a, by_segment, b, wave, lane, key, bad);
     for (int j = threadIdx.x; j < NK; j += kThreads)
         hist[j] = 0;
     __syncthreads();
@@ -181,7 +191,13 @@ __global__ __launch_bounds__(kThreads) void permute_rank_kernel(PermuteArgs a)
     }
 
     int key[kIters];
-    load_keys(a, by_segment, b, wave, lane, key);
+    int bad;
+    load_keys(a, by_segment, b, wave, lane, key, bad);
+    // report bad values: one vector atomic per wave that met any
+    const unsigned long long bad_id = __ballot((bad & MOE_LORA_FLAG_EXPERT_ID) != 0);
+    const unsigned long long bad_ad = __ballot((bad & MOE_LORA_FLAG_ADAPTER) != 0);
+    if ((bad_id | bad_ad) && lane == 0 && a.flags)
+        atomicOr(a.flags, (bad_id ? MOE_LORA_FLAG_EXPERT_ID : 0) | (bad_ad ? MOE_LORA_FLAG_ADAPTER : 0));
 
     // 1. per-wave histograms of the block's slots
     for (int j = tid; j < kWaves * NK; j += kThreads)

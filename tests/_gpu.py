@@ -69,7 +69,8 @@ class SideStream:
 
 
 def run_forward(cfg, inputs, *, use_logits=True, topk=None, mapping="given",
-                routing=False, layer=None, out=None, workspace=None, side=None):
+                routing=False, layer=None, out=None, workspace=None, side=None,
+                input_flags=None):
     """Forward through the C ABI; returns (out numpy float64, routing numpy dict | None)."""
     shape, lay = layer if layer is not None else binding.layer_from_host(cfg, inputs)
     kw = {}
@@ -92,7 +93,7 @@ def run_forward(cfg, inputs, *, use_logits=True, topk=None, mapping="given",
     if side is not None:
         kw.update(side.kwargs())
     o = binding.forward(shape, lay["hidden"], lay["w13_packed"], lay["w2_packed"], out=out,
-                        workspace=workspace, routing=r, **kw)
+                        workspace=workspace, routing=r, input_flags=input_flags, **kw)
     torch.cuda.synchronize()
     rout = None if r is None else {k: v.cpu().numpy() for k, v in r.items()}
     return bf16_to_np(o), rout

@@ -5,6 +5,7 @@ No test here enqueues device work.  Every call below either is pure host code
 call is made.
 """
 import ctypes
+import re
 import os
 
 import pytest
@@ -29,6 +30,30 @@ def test_exports_every_declared_symbol(lib):
             "moe_lora_pack_weights", "moe_lora_strerror"} <= set(names)
     for name in names:
         assert hasattr(lib, name), f"{name} declared in moe_lora.h but not exported"
+
+
+def _header_struct_fields(name):
+    text = open(binding.HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (name, name), text, re.S).group(1)
+    return [re.search(r"(\w+)\s*;", d).group(1) for d in body.split(";") if d.strip()
+            for d in [d + ";"]]
+
+
+@pytest.mark.parametrize("cname,cls", [("moe_lora_inputs", "Inputs"),
+                                        ("moe_lora_routing", "Routing")])
+def test_ctypes_structs_match_header(cname, cls):
+    """The binding's ctypes structs list the header's fields in the header's
+    order (every field is pointer-sized)."""
+    fields = _header_struct_fields(cname)
+    assert fields == [n for n, _ in getattr(binding, cls)._fields_]
+
+
+def test_flag_bits_match_header():
+    text = open(binding.HEADER_PATH).read()
+    defs = dict(re.findall(r"#define (MOE_LORA_FLAG_\w+)\s+(\d+)", text))
+    assert int(defs["MOE_LORA_FLAG_EXPERT_ID"]) == binding.FLAG_EXPERT_ID
+    assert int(defs["MOE_LORA_FLAG_ADAPTER"]) == binding.FLAG_ADAPTER
 
 
 def test_strerror(lib):
@@ -78,7 +103,7 @@ def _inputs(**over):
                 w13_packed=_fake(), w2_packed=_fake(), lora_a_gate_up=_fake(),
                 lora_b_gate_up=_fake(), lora_a_down=_fake(), lora_b_down=_fake(),
                 token_lora_mapping=_fake(), stage_events=None, expert_out=None,
-                side_stream=None, fork_event=None, join_event=None)
+                side_stream=None, fork_event=None, join_event=None, input_flags=None)
     base.update(over)
     return binding.Inputs(*[base[n] for n, _ in binding.Inputs._fields_])
 

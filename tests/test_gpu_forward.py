@@ -138,6 +138,53 @@ def test_topk_passthrough_with_invalid_slots():
     assert np.all(got[5] == 0)
 
 
+def test_input_flags_report_bad_ids_and_adapters():
+    """Bad device-side values are treated as 'none' (never fault) and are
+    reported in the caller's flag word, ORed in and never cleared."""
+    announce("forward/route: input flags")
+    cfg = MID
+    inp = make_inputs(cfg)
+    ids, w = oracle.route(inp["logits"], cfg.top_k)
+    w32 = w.astype(np.float32)
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    # clean inputs (logits and given top-k): no flag
+    run_forward(cfg, inp, input_flags=flags)
+    run_forward(cfg, inp, use_logits=False, topk=(ids, w32), input_flags=flags)
+    assert int(flags.item()) == 0
+    # -1 is the documented 'no expert' marker, not a bad id
+    ids_m1 = ids.copy()
+    ids_m1[2, 0] = -1
+    run_forward(cfg, inp, use_logits=False, topk=(ids_m1, w32), input_flags=flags)
+    assert int(flags.item()) == 0
+    # ids outside [-1, E): flagged, and the result is that of 'no expert'
+    bad_ids = ids.copy()
+    bad_ids[0, 1] = cfg.num_experts
+    bad_ids[4, 0] = -7
+    got, _ = run_forward(cfg, inp, use_logits=False, topk=(bad_ids, w32), input_flags=flags)
+    assert int(flags.item()) == binding.FLAG_EXPERT_ID
+    as_none = bad_ids.copy()
+    as_none[0, 1] = -1
+    as_none[4, 0] = -1
+    _compare(cfg, inp, got, topk_ids=as_none, topk_weights=w32.astype(np.float64))
+    # adapters outside [-1, L): flagged (ORed onto the earlier bit); the
+    # oracle counts them as -1
+    inp_bad = dict(inp)
+    mapping = np.asarray(inp["mapping"], np.int32).copy()
+    mapping[1] = cfg.num_loras
+    mapping[6] = -4
+    inp_bad["mapping"] = mapping
+    got, _ = run_forward(cfg, inp_bad, input_flags=flags)
+    assert int(flags.item()) == binding.FLAG_EXPERT_ID | binding.FLAG_ADAPTER
+    _compare(cfg, inp_bad, got)
+    # routing alone reports through its own pointer
+    flags.zero_()
+    shape, lay = binding.layer_from_host(cfg, inp_bad)
+    binding.route(shape, router_logits=lay["router_logits"],
+                  token_lora_mapping=lay["token_lora_mapping"], input_flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == binding.FLAG_ADAPTER
+
+
 def test_expert_parallel_offsets_and_shard_sum():
     full_cfg = MID.replace(name="ep_full", num_experts=16, local_num_experts=16)
     inp_full = make_inputs(full_cfg)

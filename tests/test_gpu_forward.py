@@ -47,6 +47,17 @@ WIDE_R8 = WIDE.replace(name="wide_r8", num_tokens=520, num_loras=1, rank_gate_up
 # multiples of 8 (zero-padded shrink rows; the 16-row GEMM tiles)
 SHRINK_R20 = LayerConfig("shrink_r20", 300, 256, 96, 8, 2, 0, 8, 2, 20, 12, seed=37,
                          mapping="uniform", sigma_lora_a=0.2, sigma_lora_b=0.2)
+# Every token carries an adapter (mapping "runs"), so the segments average
+# exactly n / (L * E_l) rows: 20 (the many-row shrink with two M tiles per
+# pass), 12 (the few-row shrink with two M tiles), and 25 with rank 80 (above
+# the many-row kernel's limit: the few-row shrink with three M tiles and four
+# rank tiles per pass).
+SHRINK_MT2 = LayerConfig("shrink_mt2", 160, 256, 96, 8, 2, 0, 8, 2, 24, 16, seed=38,
+                         mapping="runs", run_length=80, sigma_lora_a=0.2, sigma_lora_b=0.2)
+SHRINK_FEW2 = LayerConfig("shrink_few2", 96, 256, 96, 8, 2, 0, 8, 2, 16, 16, seed=39,
+                          mapping="runs", run_length=48, sigma_lora_a=0.2, sigma_lora_b=0.2)
+SHRINK_FEW3 = LayerConfig("shrink_few3", 200, 256, 96, 8, 2, 0, 8, 2, 80, 72, seed=40,
+                          mapping="runs", run_length=100, sigma_lora_a=0.1, sigma_lora_b=0.1)
 
 
 def _compare(cfg, inp, got, tokens=None, **kw):
@@ -82,7 +93,7 @@ def test_prefill_sampled_tokens():
 
 
 @pytest.mark.parametrize("cfg", [MID, MID_R64, MID_EP, BIG_ROWS, TINY_AMP, WIDE, WIDE_R8,
-                                 WIDE_H128, SHRINK_R20],
+                                 WIDE_H128, SHRINK_R20, SHRINK_MT2, SHRINK_FEW2, SHRINK_FEW3],
                          ids=lambda c: c.name)
 def test_small_shapes_and_lora_delta(cfg):
     announce(f"forward {cfg.name}")

@@ -139,9 +139,14 @@ def algorithmic_cost(cfg, ids, mapping):
 PROFILES = os.path.join(ROOT, "profiles")
 GEMM_SOURCES = ["mixture_experts_layer_up_amd/csrc/expert_gemm.hip",
                 "mixture_experts_layer_up_amd/csrc/expert_gemm_wide.hip",
+                "mixture_experts_layer_up_amd/csrc/mfma_pipeline.h",
+                "mixture_experts_layer_up_amd/csrc/lora_shrink_rows.h",
                 "mixture_experts_layer_up_amd/csrc/device_common.h",
                 "mixture_experts_layer_up_amd/csrc/lds_dma.h",
                 "mixture_experts_layer_up_amd/csrc/kernels.h"]
+# the timed region records the dominant kernel's event pair on every
+# EVENT_EVERY-th step
+EVENT_EVERY = 4
 DOMINANT = {"decode": "expert_gemm_kernel<1, 1, true, true>", "prefill": "expert_gemm_wide_kernel<true>"}
 
 
@@ -356,19 +361,21 @@ def main():
     nstage = len(binding.STAGE_NAMES)
     stream = torch.cuda.current_stream().cuda_stream
 
-    # The timed region: K steps launched from the host.  Each step records
-    # only the two stage events around the dominant kernel (the gate_up
-    # GEMM), whose elapsed time is that kernel's live duration; every
-    # recorded event costs stream time, so the other boundaries are left out.
+    # The timed region: K steps launched from the host.  Every EVENT_EVERY-th
+    # step records the two stage events around the dominant kernel (the
+    # gate_up GEMM), whose elapsed time is that kernel's live duration; every
+    # recorded event costs stream time (two cost ~5 us), so the other
+    # boundaries are left out and the sampled steps are spread evenly.
     gi = binding.STAGE_NAMES.index("gemm_gate_up_swiglu")  # between events gi, gi + 1
-    kev = [hip.create(2) for _ in range(K)]
+    kev = [hip.create(2) for _ in range((K + EVENT_EVERY - 1) // EVENT_EVERY)]
 
     def dominant_events(pair):
         ev = [None] * binding.NUM_STAGE_EVENTS
         ev[gi], ev[gi + 1] = pair
         return ev
 
-    plan = [dominant_events(p) for p in kev]
+    plan = [dominant_events(kev[s_ // EVENT_EVERY]) if s_ % EVENT_EVERY == 0 else None
+            for s_ in range(K)]
     start, end = hip.create(2)
     log(f"[bench] timing {K} steps")
     torch.cuda.synchronize()
@@ -381,7 +388,7 @@ def main():
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
     ms_per_step = hip.elapsed_ms(start, end) / K
-    gate_up_ms = sum(hip.elapsed_ms(a, b) for a, b in kev) / K
+    gate_up_ms = sum(hip.elapsed_ms(a, b) for a, b in kev) / len(kev)
     for p in kev:
         hip.destroy(p)
     hip.destroy([start, end])
@@ -503,9 +510,10 @@ def main():
                   "touched_lora_pairs": cost["touched_lora_pairs"],
                   "local_slots": cost["local_slots"]},
         "stages_us": {n: float(v * 1e3) for n, v in zip(binding.STAGE_NAMES, stage_ms)},
-        "timing": "K host-launched steps between two HIP events on the launch stream; in each "
-                  "step two more events bracket the gate_up GEMM (roofline kernel_us); "
-                  "stages_us comes from a separate pass with all seven stage events",
+        "timing": "K host-launched steps between two HIP events on the launch stream; in every "
+                  f"{EVENT_EVERY}th step two more events bracket the gate_up GEMM (roofline "
+                  "kernel_us, the mean over those launches); stages_us comes from a separate "
+                  "pass with all seven stage events",
         "wall_ms_per_step": wall_s * 1e3 / K,
         "graph_replay": None if graph_ms is None else {
             "ms_per_step": graph_ms, "tokens_per_s": cfg.num_tokens / (graph_ms / 1e3),

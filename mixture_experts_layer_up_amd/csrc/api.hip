@@ -129,7 +129,8 @@ int enqueue_routing(const moe_lora_shape *s, const float *logits, const float *b
                     const int32_t *topk_ids, const int32_t *mapping, int32_t *flags,
                     const RoutingPtrs &r, int32_t *block_counts, hipStream_t st,
                     int4 *tiles = nullptr, int tile_rows = 0, int max_tiles = 0,
-                    int32_t *tile_count = nullptr, void *zeros = nullptr)
+                    int32_t *tile_count = nullptr, void *zeros = nullptr,
+                    const ShrinkArgs *fuse_shrink = nullptr, bool *shrink_done = nullptr)
 {
     if (logits) {
         RouteArgs ra{logits, r.ids, r.weights, s->num_tokens, s->num_experts, s->top_k,
@@ -159,6 +160,13 @@ int enqueue_routing(const moe_lora_shape *s, const float *logits, const float *b
     pa.block_counts = block_counts;
     pa.E = s->num_experts;
     pa.flags = flags;
+    // the gate_up shrink joins the permute's launch when the shapes allow it
+    if (fuse_shrink && permute_shrink_fusable(pa, *fuse_shrink)) {
+        ShrinkArgs sa = *fuse_shrink;
+        MOE_TRY(check(launch_permute_shrink(pa, sa, st)));
+        *shrink_done = true;
+        return MOE_LORA_OK;
+    }
     return check(launch_permute(pa, st));
 }
 
@@ -365,27 +373,32 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
                              : reinterpret_cast<uint16_t *>(ws + lay.y);
     const uint16_t *hidden = static_cast<const uint16_t *>(in->hidden);
 
-    MOE_TRY(record(ev, 0, st));
-    int4 *tiles = reinterpret_cast<int4 *>(ws + lay.tiles);
-    void *zeros = ws + lay.zeros;
-    int32_t *tile_count = reinterpret_cast<int32_t *>(ws + lay.tile_count);
-    int32_t *flags = in->input_flags ? in->input_flags : routing ? routing->input_flags : nullptr;
-    MOE_TRY(enqueue_routing(shape, in->router_logits, in->routing_bias, in->topk_ids,
-                            in->token_lora_mapping, flags, r,
-                            reinterpret_cast<int32_t *>(ws + lay.perm_scratch), st,
-                            tiles, lay.tile_rows, lay.max_tiles, tile_count, zeros));
-    MOE_TRY(record(ev, 1, st));
-
     // Two-stream schedule: the gate_up shrink runs on the side stream while
     // the main-K part of the gate_up GEMM runs here; the expand waits for it.
     const bool two_stream = gu && in->side_stream != nullptr;
     hipStream_t side = static_cast<hipStream_t>(in->side_stream);
     hipEvent_t fork = static_cast<hipEvent_t>(in->fork_event);
     hipEvent_t join = static_cast<hipEvent_t>(in->join_event);
-    if (gu) {
-        ShrinkArgs sa{hidden, 1, H, static_cast<const uint16_t *>(in->lora_a_gate_up),
-                      rg, round8(rg), L, E_l, k, r.seg_offsets, r.seg_slots, r.exp2perm, s_gu,
-                      T * k, shape->lora_shared_outer};
+    const ShrinkArgs sa_gu{hidden, 1, H, static_cast<const uint16_t *>(in->lora_a_gate_up),
+                           rg, round8(rg), L, E_l, k, r.seg_offsets, r.seg_slots, r.exp2perm,
+                           s_gu, T * k, shape->lora_shared_outer};
+
+    MOE_TRY(record(ev, 0, st));
+    int4 *tiles = reinterpret_cast<int4 *>(ws + lay.tiles);
+    void *zeros = ws + lay.zeros;
+    int32_t *tile_count = reinterpret_cast<int32_t *>(ws + lay.tile_count);
+    int32_t *flags = in->input_flags ? in->input_flags : routing ? routing->input_flags : nullptr;
+    // one stream: the gate_up shrink may run in the permute's launch
+    bool shrink_done = false;
+    MOE_TRY(enqueue_routing(shape, in->router_logits, in->routing_bias, in->topk_ids,
+                            in->token_lora_mapping, flags, r,
+                            reinterpret_cast<int32_t *>(ws + lay.perm_scratch), st,
+                            tiles, lay.tile_rows, lay.max_tiles, tile_count, zeros,
+                            gu && !two_stream ? &sa_gu : nullptr, &shrink_done));
+    MOE_TRY(record(ev, 1, st));
+
+    if (gu && !shrink_done) {
+        const ShrinkArgs &sa = sa_gu;
         if (two_stream) {
             MOE_TRY(check(hipEventRecord(fork, st)));
             MOE_TRY(check(hipStreamWaitEvent(side, fork, 0)));

@@ -40,11 +40,11 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "lora_shrink_rows.h"
+#include "mfma_pipeline.h"
 
 namespace moe_lora {
 namespace {
-
-constexpr int kNS = 4;  // 16-column N tiles per block (64 columns)
 
 // Tuning knobs of the decode-shaped (16-row tile) GEMM: K chunks per
 // pipeline stage, and the minimum waves per SIMD the register budget targets.
@@ -54,114 +54,6 @@ constexpr int kNS = 4;  // 16-column N tiles per block (64 columns)
 #ifndef MOE_LORA_DECODE_WAVES
 #define MOE_LORA_DECODE_WAVES 5
 #endif
-
-template <int MT>
-struct Part {
-    static constexpr int kRows = MT * 16;
-    static constexpr int kStride = kNS * 16 + 4;
-    static constexpr int kWaveFloats = kRows * kStride;
-    static constexpr int kFloats = 4 * kWaveFloats;
-};
-
-template <int MT, int NS>
-__device__ __forceinline__ void zero_acc(f32x4 (&acc)[MT][NS])
-{
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int n = 0; n < NS; ++n)
-            acc[m][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-}
-
-// Write this wave's accumulators as [row][col] fp32 partials (col < 16 * NS).
-template <int MT, int NS>
-__device__ __forceinline__ void store_partials(float *part, const f32x4 (&acc)[MT][NS],
-                                               int n_mt, int wave, int lane)
-{
-    float *pw = part + wave * Part<MT>::kWaveFloats;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        if (m < n_mt) {
-#pragma unroll
-            for (int n = 0; n < NS; ++n) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    pw[(m * 16 + 4 * (lane >> 4) + i) * Part<MT>::kStride + n * 16 + (lane & 15)] =
-                        acc[m][n][i];
-            }
-        }
-    }
-}
-
-template <int MT>
-__device__ __forceinline__ float sum_partials(const float *part, int row, int col)
-{
-    constexpr int W = Part<MT>::kWaveFloats;
-    const int o = row * Part<MT>::kStride + col;
-    return (part[o] + part[W + o]) + (part[2 * W + o] + part[3 * W + o]);
-}
-
-template <int MT, int NS, int CH>
-struct Stage {
-    u32x4 b[CH][NS];
-    u32x4 a[CH][MT];
-    bool am[CH][MT];  // applied to a[][] only when the MFMA consumes it
-};
-
-// Two-stage pipeline over virtual chunks [0, nv).  load_b(vc, b[NS]) and
-// load_a(vc, a[MT], am[MT]) fill one chunk's operands (am: keep-mask of each A
-// fragment, applied at the MFMA so that no load result is consumed early);
-// s0.b may already hold the first stage's B operands (b0_ready).
-template <int MT, int NS, int CH, typename LoadB, typename LoadA>
-__device__ __forceinline__ void run_pipeline(f32x4 (&acc)[MT][NS], int nv, int n_mt,
-                                             Stage<MT, NS, CH> &s0, Stage<MT, NS, CH> &s1,
-                                             bool b0_ready, LoadB load_b, LoadA load_a)
-{
-    if (nv <= 0)
-        return;
-    auto load_stage = [&](Stage<MT, NS, CH> &st, int vc0, bool with_b) {
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int vc = min(vc0 + c, nv - 1);
-            if (with_b)
-                load_b(vc, st.b[c]);
-            load_a(vc, st.a[c], st.am[c]);
-        }
-    };
-    auto compute_stage = [&](const Stage<MT, NS, CH> &st, int vc0) {
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            if (vc0 + c < nv) {
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    if (m < n_mt) {
-                        const u32x4 av = keep_if(st.a[c][m], st.am[c][m]);
-#pragma unroll
-                        for (int n = 0; n < NS; ++n)
-                            acc[m][n] = mfma_16x16x32(av, st.b[c][n], acc[m][n]);
-                    }
-                }
-            }
-        }
-    };
-    load_stage(s0, 0, !b0_ready);
-    int vc0 = 0;
-    while (true) {
-        const int v1 = vc0 + CH;
-        if (v1 < nv)
-            load_stage(s1, v1, true);
-        compute_stage(s0, vc0);
-        if (v1 >= nv)
-            break;
-        const int v2 = v1 + CH;
-        if (v2 < nv)
-            load_stage(s0, v2, true);
-        compute_stage(s1, v1);
-        if (v2 >= nv)
-            break;
-        vc0 = v2;
-    }
-}
 
 template <int MT, int CH, bool kGated, bool kRank8>
 __global__ __launch_bounds__(256, MT == 1 ? (kRank8 ? MOE_LORA_DECODE_WAVES : 3) : 1) void expert_gemm_kernel(GemmArgs a)
@@ -355,110 +247,21 @@ __global__ __launch_bounds__(256, MT == 1 ? (kRank8 ? MOE_LORA_DECODE_WAVES : 3)
     }
 }
 
-// LoRA shrink: S[x, 0:rp] = A[l, e] x_row for the slots x of one virtual
-// expert (adapter l, local expert e) per block, 16 * MT rows per pass; q >= r
-// is written as 0.  S is indexed by slot, so the gate_up shrink (rows = the
-// slots' tokens) needs no permutation lookup at all.  The stack A[l, e]
-// (r x K) is K-contiguous per rank row, which is exactly the per-lane B
-// operand layout of the MFMA (8 consecutive K values of one column q).  NS
-// 16-column tiles of q per pass over N; the 4 waves split K.
+// LoRA shrink over the (adapter, expert) segments the permute wrote: one
+// block per virtual expert, its rows from the segment's slot list.
 template <int NS, int CH, int MT>
 __global__ __launch_bounds__(256, 2) void lora_shrink_kernel(ShrinkArgs a)
 {
-    constexpr int kRows = 16 * MT;
     __shared__ float part[Part<MT>::kFloats];
-    __shared__ int row_slot[kRows];
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = wave_id();
+    __shared__ int row_slot[16 * MT];
     const int seg = blockIdx.x;  // = l * E_l + e, the stack's own order
-    const int KC = a.K >> 5;
-    const int kc_per = (KC + 3) >> 2;
-    const int kbeg = min(KC, wave * kc_per);
-    const int nm = min(KC, kbeg + kc_per) - kbeg;
-    const int n_nt = (a.r + 15) >> 4;
-    const int stack = a.a_shared ? seg / a.E_l : seg;  // shared: one stack per adapter
-    const uint16_t *abase = a.A + (size_t)stack * a.r * a.K + (lane >> 4) * 8;
-
-    Stage<MT, NS, CH> s0, s1;
-    auto load_b_nt = [&](int nt0, int vc, u32x4 (&b)[NS]) {
-        const int kc = kbeg + vc;
-#pragma unroll
-        for (int n = 0; n < NS; ++n) {
-            const int q = (nt0 + n) * 16 + (lane & 15);
-            // q >= r reads a clamped valid row; those output columns are not stored
-            b[n] = load16_stream(abase + (size_t)min(q, a.r - 1) * a.K + kc * 32);
-        }
-    };
     const int beg = a.seg_offsets[seg];
     const int n_rows = a.seg_offsets[seg + 1] - beg;
     if (n_rows <= 0)
         return;
-    // the stack's first stage does not depend on the rows: issue it before
-    // the dependent row lookups
-    const bool early = nm >= CH;
-    if (early) {
-#pragma unroll
-        for (int c = 0; c < CH; ++c)
-            load_b_nt(0, c, s0.b[c]);
-    }
-
-    bool first = true;
-    for (int pass = 0; pass < n_rows; pass += kRows) {
-        const int rows = min(kRows, n_rows - pass);
-        const int n_mt = (rows + 15) >> 4;
-        // this lane's row in each M tile (past the segment: its last row,
-        // computed but never stored)
-        const uint16_t *aptr[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const int x = a.seg_slots[beg + min(pass + m * 16 + (lane & 15), n_rows - 1)];
-            const int xrow = a.gather_by_token ? x / a.k : a.exp2perm[x];
-            aptr[m] = a.X + (size_t)xrow * a.K + (lane >> 4) * 8;
-        }
-        lds_barrier();  // the previous pass's epilogue is done with row_slot
-        if (tid < kRows)
-            row_slot[tid] = a.seg_slots[beg + min(pass + tid, n_rows - 1)];
-        auto load_a = [&](int vc, u32x4 (&av)[MT], bool (&am)[MT]) {
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                if (m < n_mt) {
-                    av[m] = load16(aptr[m] + (kbeg + vc) * 32);
-                    am[m] = true;
-                }
-            }
-        };
-        for (int nt0 = 0; nt0 < n_nt; nt0 += NS) {
-            auto load_b = [&](int vc, u32x4 (&b)[NS]) { load_b_nt(nt0, vc, b); };
-            f32x4 acc[MT][NS];
-            zero_acc(acc);
-            run_pipeline<MT, NS, CH>(acc, nm, n_mt, s0, s1, first && early, load_b, load_a);
-            first = false;
-
-            lds_barrier();  // the previous epilogue is done with `part`
-            store_partials<MT, NS>(part, acc, n_mt, wave, lane);
-            lds_barrier();
-
-            const int groups = min(NS, n_nt - nt0) * 2;  // 8-wide q groups
-            for (int item = tid; item < rows * groups; item += 256) {
-                const int row = item / groups;
-                const int g = item - row * groups;
-                const int q0 = nt0 * 16 + g * 8;
-                if (q0 >= a.rp)
-                    continue;
-                uint32_t packed[4];
-#pragma unroll
-                for (int i = 0; i < 8; i += 2) {
-                    const float v0 = (q0 + i < a.r) ? sum_partials<MT>(part, row, g * 8 + i) : 0.0f;
-                    const float v1 =
-                        (q0 + i + 1 < a.r) ? sum_partials<MT>(part, row, g * 8 + i + 1) : 0.0f;
-                    packed[i >> 1] = float_to_bf16_bits(v0) | (float_to_bf16_bits(v1) << 16);
-                }
-                store16(a.S + (size_t)row_slot[row] * a.rp + q0,
-                        u32x4{packed[0], packed[1], packed[2], packed[3]});
-            }
-        }
-    }
+    const int stack = a.a_shared ? seg / a.E_l : seg;  // shared: one stack per adapter
+    shrink_rows<NS, CH, MT>(a, stack, n_rows, [&](int i) { return a.seg_slots[beg + i]; },
+                            part, row_slot);
 }
 
 template <int MT, int CH, bool kGated>
@@ -504,18 +307,33 @@ hipError_t launch_gemm_down(const GemmArgs &a, hipStream_t s)
                                           : launch_gemm_wide(a, false, s);
 }
 
+bool shrink_uses_wide(const ShrinkArgs &a)
+{
+    // rows per (adapter, expert) segment, on average, when every slot
+    // carries an adapter; segments of tens of rows take the direct-load
+    // kernel (lora_shrink_wide.hip)
+    const int blocks = a.L * a.E_l;
+    const int mean = blocks > 0 ? (a.n_slots + blocks - 1) / blocks : 0;
+    return mean >= 16 && shrink_wide_supported(a.r);
+}
+
+int shrink_row_tiles(const ShrinkArgs &a)
+{
+    // rows per pass from the mean rows per segment: one pass covers most
+    // segments
+    const int blocks = a.L * a.E_l;
+    const int mean = blocks > 0 ? (a.n_slots + blocks - 1) / blocks : 0;
+    return mean <= 8 ? 1 : mean <= 24 ? 2 : 3;
+}
+
 hipError_t launch_shrink(const ShrinkArgs &a, hipStream_t s)
 {
     const int blocks = a.L * a.E_l;
     if (blocks <= 0 || a.r <= 0)
         return hipSuccess;
-    // rows per pass from the mean rows per (adapter, expert) segment when
-    // every slot carries an adapter: one pass covers most segments
-    const int mean = (a.n_slots + blocks - 1) / blocks;
-    // segments of tens of rows: the direct-load kernel (lora_shrink_wide.hip)
-    if (mean >= 16 && shrink_wide_supported(a.r))
-        return launch_shrink_wide(a, mean, s);
-    const int mt = mean <= 8 ? 1 : mean <= 24 ? 2 : 3;
+    if (shrink_uses_wide(a))
+        return launch_shrink_wide(a, (a.n_slots + blocks - 1) / blocks, s);
+    const int mt = shrink_row_tiles(a);
     if (a.r <= 16) {
         if (mt == 1)
             hipLaunchKernelGGL((lora_shrink_kernel<1, 8, 1>), dim3(blocks), dim3(256), 0, s, a);

@@ -149,6 +149,14 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t s);
 hipError_t launch_permute(const PermuteArgs &a, hipStream_t s);
 hipError_t launch_pack(const PackArgs &a, hipStream_t s);
 hipError_t launch_shrink(const ShrinkArgs &a, hipStream_t s);
+// launch_shrink's choices: the many-row kernel, else the few-row kernel with
+// 16 * shrink_row_tiles(a) rows per pass
+bool shrink_uses_wide(const ShrinkArgs &a);
+int shrink_row_tiles(const ShrinkArgs &a);
+// The permute (one slot block) and the gate_up shrink (few-row kernel) in one
+// launch; permute_shrink_fusable says whether the shapes allow it.
+bool permute_shrink_fusable(const PermuteArgs &pa, const ShrinkArgs &sa);
+hipError_t launch_permute_shrink(const PermuteArgs &pa, const ShrinkArgs &sa, hipStream_t s);
 // the shrink for segments of many rows: rank r <= 64, mean_rows per segment
 bool shrink_wide_supported(int r);
 hipError_t launch_shrink_wide(const ShrinkArgs &a, int mean_rows, hipStream_t s);

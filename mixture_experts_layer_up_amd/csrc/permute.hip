@@ -25,6 +25,7 @@
 // histogram is the whole one and the count kernel is skipped.
 #include "device_common.h"
 #include "kernels.h"
+#include "lora_shrink_rows.h"
 #include "moe_lora.h"
 
 namespace moe_lora {
@@ -35,6 +36,7 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kIters = kPermuteSlotsPerBlock / kThreads;  // 64-slot groups per wave, at most
 constexpr int kMaxKeys = 8192;                            // local experts, or adapters * local experts
 constexpr int kMaxExperts = 1024;
+constexpr int kFusedKeys = 1024;                          // keys of the permute fused with the shrink
 
 // key of a slot from its expert id and its token's adapter l (-1: none)
 __device__ __forceinline__ int key_from(const PermuteArgs &a, bool by_segment, int id, int l)
@@ -160,18 +162,19 @@ __global__ __launch_bounds__(kThreads) void permute_count_kernel(PermuteArgs a)
         dst[j] = j < NK ? hist[j] : 0;
 }
 
-__global__ __launch_bounds__(kThreads) void permute_rank_kernel(PermuteArgs a)
+// The rank pass of slot block g for one key type.  kKeys bounds the keys
+// (E_l, or L * E_l) and kExperts the local experts: they size the LDS tables.
+template <int kKeys, int kExperts>
+__device__ __forceinline__ void permute_rank_body(const PermuteArgs &a, bool by_segment, int g)
 {
-    __shared__ int table[kWaves * kMaxKeys];  // per-wave counts, then per-wave running positions
-    __shared__ int exp_first[kMaxExperts];    // expert offsets and counts, for the work list
-    __shared__ int exp_rows[kMaxExperts];
+    __shared__ int table[kWaves * kKeys];  // per-wave counts, then per-wave running positions
+    __shared__ int exp_first[kExperts];    // expert offsets and counts, for the work list
+    __shared__ int exp_rows[kExperts];
     __shared__ int wave_tot[kWaves];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid >> 6;
-    const bool by_segment = blockIdx.y == 1;
-    const int g = blockIdx.x;
     const int G = a.G;
     const int n = a.T * a.k;
     const int NK = by_segment ? a.L * a.E_l : a.E_l;
@@ -349,7 +352,95 @@ __global__ __launch_bounds__(kThreads) void permute_rank_kernel(PermuteArgs a)
     }
 }
 
+__global__ __launch_bounds__(kThreads) void permute_rank_kernel(PermuteArgs a)
+{
+    permute_rank_body<kMaxKeys, kMaxExperts>(a, blockIdx.y == 1, blockIdx.x);
+}
+
+// The permute and the gate_up LoRA shrink in one launch, for batches of one
+// slot block.  The shrink reads only the routing (ids, adapter mapping), not
+// the permute's output: each of its blocks owns one virtual expert (adapter
+// l, local expert e), finds its slots by scanning the ids itself and writes
+// S by slot.  So the shrink runs beside the permute instead of after it, and
+// one launch boundary goes.  Blocks 0 and 1 are the permute's two key types;
+// block 2 + l * E_l + e is virtual expert (l, e).  Requires T * k <=
+// kPermuteSlotsPerBlock and E_l, L * E_l <= kFusedKeys.
+template <int NS, int CH, int MT>
+__global__ __launch_bounds__(kThreads, 2) void permute_shrink_kernel(PermuteArgs pa, ShrinkArgs sa)
+{
+    if (blockIdx.x < 2) {
+        permute_rank_body<kFusedKeys, kFusedKeys>(pa, blockIdx.x == 1, 0);
+        return;
+    }
+    __shared__ float part[Part<MT>::kFloats];
+    __shared__ int row_slot[16 * MT];
+    __shared__ int list[kPermuteSlotsPerBlock];
+    __shared__ int wave_tot[kWaves];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid >> 6;
+    const int seg = blockIdx.x - 2;
+    const int l = seg / pa.E_l;
+    const int want = pa.off + (seg - l * pa.E_l);  // global id of expert e
+    const int n = pa.T * pa.k;
+    // slots 4 tid .. 4 tid + 3; all loads issued before any is used.  A slot
+    // belongs here when its id is expert e and its token's adapter is l (so
+    // out-of-range ids and adapters never match, as in the permute's keys).
+    int id[4], ad[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int x = 4 * tid + i;
+        id[i] = x < n ? pa.topk_ids[x] : -1;
+        ad[i] = (x < n && pa.mapping) ? pa.mapping[x / pa.k] : -1;
+    }
+    int hit = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        hit |= (4 * tid + i < n && id[i] == want && ad[i] == l) ? 1 << i : 0;
+    const int c = __popc(hit);
+    int total;
+    int pos = block_scan(c, lane, wave, wave_tot, total) - c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if ((hit >> i) & 1)
+            list[pos++] = 4 * tid + i;  // ascending slot order
+    if (total == 0)
+        return;
+    __syncthreads();  // list
+    const int stack = sa.a_shared ? l : seg;
+    shrink_rows<NS, CH, MT>(sa, stack, total, [&](int i) { return list[i]; }, part, row_slot);
+}
+
 } // namespace
+
+bool permute_shrink_fusable(const PermuteArgs &pa, const ShrinkArgs &sa)
+{
+    return pa.G == 1 && pa.T * pa.k <= kPermuteSlotsPerBlock && pa.E_l <= kFusedKeys &&
+           pa.L * pa.E_l <= kFusedKeys && sa.r > 0 && sa.L == pa.L && sa.E_l == pa.E_l &&
+           !shrink_uses_wide(sa);
+}
+
+hipError_t launch_permute_shrink(const PermuteArgs &pa, const ShrinkArgs &sa, hipStream_t s)
+{
+    const dim3 grid(2 + pa.L * pa.E_l);
+    const int mt = shrink_row_tiles(sa);
+    if (sa.r <= 16) {
+        if (mt == 1)
+            hipLaunchKernelGGL((permute_shrink_kernel<1, 8, 1>), grid, dim3(kThreads), 0, s, pa, sa);
+        else if (mt == 2)
+            hipLaunchKernelGGL((permute_shrink_kernel<1, 4, 2>), grid, dim3(kThreads), 0, s, pa, sa);
+        else
+            hipLaunchKernelGGL((permute_shrink_kernel<1, 4, 3>), grid, dim3(kThreads), 0, s, pa, sa);
+    } else {
+        if (mt == 1)
+            hipLaunchKernelGGL((permute_shrink_kernel<4, 2, 1>), grid, dim3(kThreads), 0, s, pa, sa);
+        else if (mt == 2)
+            hipLaunchKernelGGL((permute_shrink_kernel<4, 2, 2>), grid, dim3(kThreads), 0, s, pa, sa);
+        else
+            hipLaunchKernelGGL((permute_shrink_kernel<4, 2, 3>), grid, dim3(kThreads), 0, s, pa, sa);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_permute(const PermuteArgs &a, hipStream_t s)
 {

@@ -14,7 +14,9 @@ import pytest
 
 from mixture_experts_layer_up_amd import build
 
-SOURCES = [f for f in build.sources() if "expert_gemm" in f or "lora_shrink" in f]
+# every source with MFMA code (the permute launch also runs the gate_up shrink)
+SOURCES = [f for f in build.sources()
+           if "expert_gemm" in f or "lora_shrink" in f or "permute" in f]
 
 
 def _device_asm(src, tmp_path):

@@ -59,6 +59,19 @@ SHRINK_FEW2 = LayerConfig("shrink_few2", 96, 256, 96, 8, 2, 0, 8, 2, 16, 16, see
 SHRINK_FEW3 = LayerConfig("shrink_few3", 200, 256, 96, 8, 2, 0, 8, 2, 80, 72, seed=40,
                           mapping="runs", run_length=100, sigma_lora_a=0.1, sigma_lora_b=0.1)
 
+# The gate_up shrink's three launch shapes on decode-like (few-row) segments:
+# exactly 1024 slots with 128 (adapter, expert) pairs (the largest batch whose
+# shrink runs inside the permute's launch: every scan lane holds a slot);
+# 1600 slots (two permute slot blocks: a separate few-row shrink launch);
+# 64 adapters x 17 local experts = 1088 pairs (above the fused permute's key
+# tables: separate launches on a 64-slot batch).
+FUSED_FULL = LayerConfig("fused_full", 128, 256, 96, 32, 8, 0, 32, 4, 16, 16, seed=41,
+                         mapping="uniform", sigma_lora_a=0.2, sigma_lora_b=0.2)
+SPLIT_FEW = LayerConfig("split_few", 200, 256, 96, 64, 8, 0, 64, 4, 16, 16, seed=42,
+                        mapping="uniform", sigma_lora_a=0.2, sigma_lora_b=0.2)
+MANY_PAIRS = LayerConfig("many_pairs", 16, 128, 64, 17, 4, 0, 17, 64, 8, 8, seed=43,
+                         mapping="uniform", sigma_lora_a=0.3, sigma_lora_b=0.3)
+
 
 def _compare(cfg, inp, got, tokens=None, **kw):
     ref = oracle.forward(cfg, inp, tokens=tokens, **kw)
@@ -93,7 +106,8 @@ def test_prefill_sampled_tokens():
 
 
 @pytest.mark.parametrize("cfg", [MID, MID_R64, MID_EP, BIG_ROWS, TINY_AMP, WIDE, WIDE_R8,
-                                 WIDE_H128, SHRINK_R20, SHRINK_MT2, SHRINK_FEW2, SHRINK_FEW3],
+                                 WIDE_H128, SHRINK_R20, SHRINK_MT2, SHRINK_FEW2, SHRINK_FEW3,
+                                 FUSED_FULL, SPLIT_FEW, MANY_PAIRS],
                          ids=lambda c: c.name)
 def test_small_shapes_and_lora_delta(cfg):
     announce(f"forward {cfg.name}")

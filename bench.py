@@ -217,6 +217,40 @@ def summarize_counters(fetch_csv: str, write_csv: str, out_md: str, command: str
         f.write("\n".join(lines) + "\n")
 
 
+def summarize_mfma(csv_path: str, out_md: str, command: str):
+    """MfmaUtil (MFMA busy cycles over GRBM_GUI_ACTIVE x SIMDs, percent) and
+    MfmaFlopsBF16 (bf16 MFMA operations x 512) per dispatch, median per
+    kernel; TFLOP/s over the same dispatches' durations."""
+    import csv
+    import statistics
+    util, flops, dur = {}, {}, {}
+    for r in csv.DictReader(open(csv_path)):
+        k = _kernel_short(r["Kernel_Name"])
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if r["Counter_Name"] == "MfmaUtil":
+            util.setdefault(k, []).append(float(r["Counter_Value"]))
+            dur.setdefault(k, []).append(d)
+        elif r["Counter_Name"] == "MfmaFlopsBF16":
+            flops.setdefault(k, []).append(float(r["Counter_Value"]))
+    lines = [f"# MFMA counters: {os.path.basename(out_md)[:-3]}", "",
+             f"command: `{command}`", "",
+             f"kernel_source_sha256: {gemm_source_hash()}", "",
+             f"peak: {MFMA_BF16_PEAK_TFLOPS:.0f} TFLOP/s dense bf16", "",
+             "| kernel | dispatches | MfmaUtil % | bf16 MFMA GFLOP per dispatch | us (counter run) | TFLOP/s | of peak |",
+             "|---|---|---|---|---|---|---|"]
+    for k in util:
+        u = statistics.median(util[k])
+        f = statistics.median(flops.get(k, [0.0]))
+        d = statistics.median(dur[k])
+        if f <= 0:
+            continue
+        tf = f / d / 1e6
+        lines.append(f"| `{k}` | {len(util[k])} | {u:.2f} | {f / 1e9:.3f} | {d:.1f} | {tf:.1f} | "
+                     f"{tf / MFMA_BF16_PEAK_TFLOPS:.3f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def traffic_from_profile(workload: str):
     """Counter-measured HBM bytes per launch of the dominant kernel, if the
     committed profile was taken on the current kernel source; else None."""
@@ -286,11 +320,16 @@ def main():
                     help="write a kernel-trace summary from rocprofv3 --stats output and exit")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
                     help="write an HBM counter summary from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_CSV", "OUT_MD"),
+                    help="write an MFMA-counter summary (rocprofv3 --pmc MfmaUtil MfmaFlopsBF16)")
     ap.add_argument("--command", default="", help="the profiling command, recorded in summaries")
     args = ap.parse_args()
 
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, command=args.command)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma, command=args.command)
         return
     if args.summarize_counters:
         kind = "prefill" if args.workload == "prefill" else "decode"

@@ -31,6 +31,7 @@
 //    tile (16 rows) skips the MFMAs of a chunk whose adapters it does not
 //    contain.  Needs rank % 8 == 0 (16-byte expand rows).
 //  * MFMA guards are scalar (wave-uniform) branches: MFMA ignores EXEC.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -51,6 +52,7 @@ constexpr int kAStageBytes = kWRows * 64;      // 176 rows x 32 bf16
 constexpr int kBStageBytes = kCons * kNTW * 1024;  // 16 MFMA B fragments
 constexpr int kStageBytes = kAStageBytes + kBStageBytes;
 constexpr int kAPerProd = (kWMT + kCons - 1) / kCons;  // A loads per producer: 3
+constexpr int kWideCUs = 256;                  // MI355X compute units (one block each)
 
 template <bool kGated>
 __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs a)
@@ -69,18 +71,24 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
     const int lane = tid & (kWave - 1);
     const int wave = wave_id();
 
-    // work item -> (expert, 256-column slab, row tile); see expert_gemm.hip
-    const int logical = xcd_balanced_item(blockIdx.x, *a.tile_count * a.n_slabs);
+    // work item -> (expert, group of slabs_per_block 256-column slabs, row
+    // tile); items are numbered as in expert_gemm.hip with slab groups in
+    // place of slabs
+    const int n_groups = (a.n_slabs + a.slabs_per_block - 1) / a.slabs_per_block;
+    const int logical = xcd_balanced_item(blockIdx.x, *a.tile_count * n_groups);
     if (logical < 0)
         return;
-    const int4 te = a.tiles[logical / a.n_slabs];
+    const int4 te = a.tiles[logical / n_groups];
     const int le = te.x;
     if (le < 0)
         return;
     const int nt = (te.z + a.tile_rows - 1) / a.tile_rows;
-    const int in_expert = logical - te.w * a.n_slabs;
-    const int slab = in_expert / nt;
-    const int sub = in_expert - slab * nt;
+    const int in_expert = logical - te.w * n_groups;
+    const int group = in_expert / nt;
+    const int sub = in_expert - group * nt;
+    // this block's slabs: slab0 .. slab0 + n_sl - 1, one after another
+    const int slab0 = group * a.slabs_per_block;
+    const int n_sl = min(a.slabs_per_block, a.n_slabs - slab0);
     const int row0 = te.y + sub * a.tile_rows;
     const int n_rows = min(a.tile_rows, te.z - sub * a.tile_rows);
     const int n_mt = (n_rows + 15) >> 4;
@@ -92,6 +100,13 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
     // chunks of this launch: main K only (phase 1), expand only (phase 2), or all
     const int vbeg = a.phase == 2 ? KC : 0;
     const int vend = a.phase == 1 ? KC : nv;
+    // The block's chunk sequence q = 0 .. nq - 1 runs the slabs in turn:
+    // slab slab0 + q / nvs, chunk vbeg + q % nvs.  Every chunk carries the same
+    // loads (the rows are the same for all slabs), so the producers' wait
+    // counts do not change across slabs, and they run on into the next slab
+    // while the consumers finish the previous one.
+    const int nvs = vend - vbeg;
+    const int nq = n_sl * nvs;
 
     // rows of this tile: slot, source row, adapter (rows past the tile
     // repeat the last row and carry no adapter)
@@ -114,12 +129,10 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
     }
     lds_barrier();  // mt_adapters
 
-    // The 64-column group g (0..3) of this slab: packed 64-column weight
-    // slab s64, present when it lies inside the N columns.
+    // The 64-column group g (0..3) of slab `slab`: packed 64-column weight
+    // slab s64(slab), present when it lies inside the N columns.
     const int NS64 = a.NT >> 2;
     const int g = wave & (kCons - 1);
-    const int s64 = slab * kCons + g;
-    const bool has_cols = s64 < NS64;
 
     if (wave >= kCons) {
         // ------------------------------------------------------------ producer
@@ -140,21 +153,16 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
             a_q[i] = q;
         }
         // B loads: the four fragments of weight slab s64 (contiguous 4 KiB
-        // per chunk), or of the LoRA B columns of its four 16-column tiles
-        const uint16_t *b_main =
-            a.Wp + ((size_t)le * NS64 + min(s64, NS64 - 1)) * (size_t)KC * 4 * 512 + lane * 8;
-        int b_col[kNTW];
-#pragma unroll
-        for (int t = 0; t < kNTW; ++t) {
-            const int nt16 = s64 * 4 + t;
-            b_col[t] = kGated ? (nt16 & 1) * a.I + (nt16 >> 1) * 16 + (lane & 15)
-                              : nt16 * 16 + (lane & 15);
-        }
+        // per chunk), or the LoRA B columns of its four 16-column tiles
         const uint16_t *zeros = a.zeros;
+        const size_t slab_elems = (size_t)KC * 4 * 512;  // one packed 64-column slab
 
-        // issue every load of chunk vc into stage st; `lean`: vc < KC
-        auto issue = [&](auto na, auto lean, int vc, int st) __attribute__((always_inline)) {
+        // issue every load of chunk vc of the block's slab si into stage st;
+        // `lean`: a main K chunk (vc < KC)
+        auto issue = [&](auto na, auto lean, int si, int vc, int st) __attribute__((always_inline)) {
             constexpr int NA = decltype(na)::value;
+            const int s64 = (slab0 + si) * kCons + g;
+            const bool has_cols = s64 < NS64;
             const uint32_t sa = smem_lds + (uint32_t)(st * kStageBytes);
             const uint32_t sb = sa + kAStageBytes + g * kNTW * 1024;
             if (decltype(lean)::value) {
@@ -164,7 +172,9 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
 #pragma unroll
                 for (int t = 0; t < kNTW; ++t) {
                     if (has_cols)  // weights are read once: streaming hint
-                        load_lds16_stream(b_main + ((size_t)vc * 4 + t) * 512, sb + t * 1024);
+                        load_lds16_stream(a.Wp + ((size_t)le * NS64 + s64) * slab_elems + lane * 8 +
+                                              ((size_t)vc * 4 + t) * 512,
+                                          sb + t * 1024);
                     else
                         load_lds16(zeros, sb + t * 1024);
                 }
@@ -184,39 +194,45 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
             const int q0 = gq - aid * a.rp;
 #pragma unroll
             for (int t = 0; t < kNTW; ++t) {
+                const int nt16 = s64 * 4 + t;
+                const int col = kGated ? (nt16 & 1) * a.I + (nt16 >> 1) * 16 + (lane & 15)
+                                       : nt16 * 16 + (lane & 15);
                 const uint16_t *p =
                     (has_cols && aid < a.L)
                         ? a.LB + (((a.lb_shared ? (size_t)aid : (size_t)aid * a.E_l + le) *
-                                       a.n_canon + b_col[t]) * a.r + q0)
+                                       a.n_canon + col) * a.r + q0)
                         : zeros;
                 load_lds16(p, sb + t * 1024);
             }
         };
-        auto issue_any = [&](auto na, int vc, int st) __attribute__((always_inline)) {
-            if (vc < KC)
-                issue(na, std::true_type{}, vc, st);
-            else
-                issue(na, std::false_type{}, vc, st);
-        };
-        // The stage of chunk vc is vc % kStages.  Chunks vbeg .. vbeg + S - 2
-        // go out first; after the barrier of chunk vc, chunk vc + S - 1 goes
-        // into the stage chunk vc - 1 has left.  Past the last chunk the last
-        // one is issued again, so the loads per chunk never change: chunk vc
+        // The stage of the block's chunk q is q % kStages.  Chunks 0 .. S - 2
+        // go out first; after the barrier of chunk q, chunk q + S - 1 goes
+        // into the stage chunk q - 1 has left.  Past the last chunk the last
+        // one is issued again, so the loads per chunk never change: chunk q
         // has landed once only the (S - 2) chunks issued after it can be
-        // outstanding.
+        // outstanding.  (si, vc): the next chunk to issue.
         auto run = [&](auto na) __attribute__((always_inline)) {
             constexpr int kLoads = decltype(na)::value + kNTW;
-            for (int d = 0; d < kStages - 1; ++d) {
-                const int vc = min(vbeg + d, vend - 1);
-                issue_any(na, vc, (vbeg + d) % kStages);
-            }
-            for (int vc = vbeg; vc < vend; ++vc) {
-                dma_wait_barrier<(kStages - 2) * kLoads>();
-                const int nvc = vc + kStages - 1;
-                if (nvc < KC)
-                    issue(na, std::true_type{}, nvc, nvc % kStages);
+            int si = 0, vc = vbeg, st = 0;
+            auto issue_next = [&]() __attribute__((always_inline)) {
+                const bool past = si >= n_sl;
+                const int s_i = past ? n_sl - 1 : si;
+                const int v_i = past ? vend - 1 : vc;
+                if (v_i < KC)
+                    issue(na, std::true_type{}, s_i, v_i, st);
                 else
-                    issue_any(na, min(nvc, vend - 1), nvc % kStages);
+                    issue(na, std::false_type{}, s_i, v_i, st);
+                st = st == kStages - 1 ? 0 : st + 1;
+                if (!past && ++vc == vend) {
+                    vc = vbeg;
+                    ++si;
+                }
+            };
+            for (int d = 0; d < kStages - 1; ++d)
+                issue_next();
+            for (int q = 0; q < nq; ++q) {
+                dma_wait_barrier<(kStages - 2) * kLoads>();
+                issue_next();
             }
             dma_drain();  // no direct load may land after the block's LDS is released
         };
@@ -230,44 +246,8 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
     }
 
     // -------------------------------------------------------------- consumer
-    f32x4 acc[kWMT][kNTW];
-#pragma unroll
-    for (int m = 0; m < kWMT; ++m)
-#pragma unroll
-        for (int t = 0; t < kNTW; ++t)
-            acc[m][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    const int a_lane_off = (lane & 15) * 64 + (((lane >> 4) ^ act_swizzle(lane & 15)) * 16);
-    // M tiles that exist (none for a column group past N), as a scalar mask
-    const uint32_t main_tiles =
-        __builtin_amdgcn_readfirstlane(has_cols ? (1u << n_mt) - 1u : 0u);
-
-    // multiply the chunk in stage st for the M tiles in `tiles`; A fragments
-    // are read two M tiles ahead of their MFMAs (a ring of three)
-    auto compute = [&](int st, uint32_t tiles) __attribute__((always_inline)) {
-        const unsigned char *sa = smem + st * kStageBytes;
-        const unsigned char *sb = sa + kAStageBytes + g * kNTW * 1024 + lane * 16;
-        u32x4 b[kNTW];
-#pragma unroll
-        for (int t = 0; t < kNTW; ++t)
-            b[t] = *reinterpret_cast<const u32x4 *>(sb + t * 1024);
-        u32x4 av[3];
-        av[0] = *reinterpret_cast<const u32x4 *>(sa + a_lane_off);
-        av[1] = *reinterpret_cast<const u32x4 *>(sa + 1024 + a_lane_off);
-#pragma unroll
-        for (int m = 0; m < kWMT; ++m) {
-            if (m + 2 < kWMT)  // rows past the tile: read, never used
-                av[(m + 2) % 3] =
-                    *reinterpret_cast<const u32x4 *>(sa + (m + 2) * 1024 + a_lane_off);
-            if (tiles & (1u << m)) {
-#pragma unroll
-                for (int t = 0; t < kNTW; ++t)
-                    acc[m][t] = mfma_16x16x32(av[m % 3], b[t], acc[m][t]);
-            }
-        }
-    };
     // M tiles holding a row of an adapter whose K block meets expand chunk vc
-    auto ext_tiles = [&](int vc) __attribute__((always_inline)) {
+    auto ext_tiles = [&](int vc, uint32_t main_tiles) __attribute__((always_inline)) {
         const int lo = ((vc - KC) * 32) / a.rp;
         const int hi = min(a.L - 1, ((vc - KC) * 32 + 31) / a.rp);
         const int span = hi - lo + 1;
@@ -279,81 +259,130 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
         return __builtin_amdgcn_readfirstlane(t & main_tiles);
     };
 
-    for (int vc = vbeg; vc < vend; ++vc) {
-        dma_wait_barrier<63>();  // chunk vc has landed; this wave's reads of vc - 1 are done
-        compute(vc % kStages, vc < KC ? main_tiles : ext_tiles(vc));
-    }
+    int st = 0;  // stage of the block's next chunk, as in the producers
+    for (int si = 0; si < n_sl; ++si) {
+        // per-lane offsets are recomputed in every slab from an opaque copy
+        // of the lane index: hoisted out of the loop they would stay live
+        // beside the 176 accumulator registers and spill
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int a_lane_off = (ln & 15) * 64 + (((ln >> 4) ^ act_swizzle(ln & 15)) * 16);
+        const int s64 = (slab0 + si) * kCons + g;
+        const bool has_cols = s64 < NS64;
+        f32x4 acc[kWMT][kNTW];
+#pragma unroll
+        for (int m = 0; m < kWMT; ++m)
+#pragma unroll
+            for (int t = 0; t < kNTW; ++t)
+                acc[m][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        // M tiles that exist (none for a column group past N), as a scalar mask
+        const uint32_t main_tiles =
+            __builtin_amdgcn_readfirstlane(has_cols ? (1u << n_mt) - 1u : 0u);
 
-    // Epilogue.  Lane holds rows 4 (lane / 16) + i of each M tile, column
-    // lane % 16 of its four tiles.  Phase 1 writes the fp32 pre-activation
-    // element by element; otherwise each M tile's bf16 outputs (SwiGLU'd for
-    // gate_up) go through this consumer's private LDS tile, 16 rows x kOut
-    // columns, and leave as 16-byte row segments.
-    if (!has_cols)
-        return;
-    const int c = lane & 15;
-    if (kGated && a.phase == 1) {
+        // multiply the chunk in stage st for the M tiles in `tiles`; A
+        // fragments are read two M tiles ahead of their MFMAs (a ring of three)
+        auto compute = [&](int stage, uint32_t tiles) __attribute__((always_inline)) {
+            const unsigned char *sa = smem + stage * kStageBytes;
+            const unsigned char *sb = sa + kAStageBytes + g * kNTW * 1024 + ln * 16;
+            u32x4 b[kNTW];
 #pragma unroll
-        for (int m = 0; m < kWMT; ++m) {
+            for (int t = 0; t < kNTW; ++t)
+                b[t] = *reinterpret_cast<const u32x4 *>(sb + t * 1024);
+            u32x4 av[3];
+            av[0] = *reinterpret_cast<const u32x4 *>(sa + a_lane_off);
+            av[1] = *reinterpret_cast<const u32x4 *>(sa + 1024 + a_lane_off);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = m * 16 + 4 * (lane >> 4) + i;
-                if (m < n_mt && r < n_rows) {
-                    const size_t p = (size_t)(row0 + r);
-#pragma unroll
-                    for (int q = 0; q < kNTW / 2; ++q) {
-                        const size_t h_at = p * 2 * a.I + (2 * s64 + q) * 16 + c;
-                        a.H[h_at] = acc[m][2 * q][i];
-                        a.H[h_at + a.I] = acc[m][2 * q + 1][i];
-                    }
-                }
-            }
-        }
-        return;
-    }
-    constexpr int kOut = kGated ? kNTW / 2 * 16 : kNTW * 16;  // output columns: 32 or 64
-    constexpr int kSeg = kOut / 8;                            // 16-byte segments per row
-    uint16_t *ot = otile[g];
-    // this consumer's output columns start at column `col0` of the output rows
-    const int col0 = kGated ? 2 * s64 * 16 : s64 * 64;
-    const int ld = kGated ? a.I : a.n_canon;
-#pragma unroll
-    for (int m = 0; m < kWMT; ++m) {
-        if (m < n_mt) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rr = 4 * (lane >> 4) + i;
-                if (kGated) {
-#pragma unroll
-                    for (int q = 0; q < kNTW / 2; ++q) {
-                        float gate = acc[m][2 * q][i], up = acc[m][2 * q + 1][i];
-                        if (a.phase == 2 && m * 16 + rr < n_rows) {
-                            const size_t h_at =
-                                (size_t)(row0 + m * 16 + rr) * 2 * a.I + (2 * s64 + q) * 16 + c;
-                            gate += a.H[h_at];
-                            up += a.H[h_at + a.I];
-                        }
-                        ot[rr * kOut + q * 16 + c] =
-                            (uint16_t)float_to_bf16_bits(silu_f32(gate) * up);
-                    }
-                } else {
+            for (int m = 0; m < kWMT; ++m) {
+                if (m + 2 < kWMT)  // rows past the tile: read, never used
+                    av[(m + 2) % 3] =
+                        *reinterpret_cast<const u32x4 *>(sa + (m + 2) * 1024 + a_lane_off);
+                if (tiles & (1u << m)) {
 #pragma unroll
                     for (int t = 0; t < kNTW; ++t)
-                        ot[rr * kOut + t * 16 + c] = (uint16_t)float_to_bf16_bits(acc[m][t][i]);
+                        acc[m][t] = mfma_16x16x32(av[m % 3], b[t], acc[m][t]);
                 }
             }
-            // one wave: its LDS operations complete in order, so the reads
-            // below see every lane's writes above
-            __builtin_amdgcn_wave_barrier();
+        };
+
+        for (int vc = vbeg; vc < vend; ++vc) {
+            dma_wait_barrier<63>();  // the chunk has landed; this wave's reads of the previous one are done
+            compute(st, vc < KC ? main_tiles : ext_tiles(vc, main_tiles));
+            st = st == kStages - 1 ? 0 : st + 1;
+        }
+
+        // Epilogue of this slab (the producers meanwhile fill the stages with
+        // the next slab's first chunks).  Lane holds rows 4 (lane / 16) + i of
+        // each M tile, column lane % 16 of its four tiles.  Phase 1 writes the
+        // fp32 pre-activation element by element; otherwise each M tile's
+        // bf16 outputs (SwiGLU'd for gate_up) go through this consumer's
+        // private LDS tile, 16 rows x kOut columns, and leave as 16-byte row
+        // segments.
+        if (!has_cols)
+            continue;
+        const int c = ln & 15;
+        if (kGated && a.phase == 1) {
 #pragma unroll
-            for (int h = 0; h < 16 * kSeg / kWave; ++h) {
-                const int e = h * kWave + lane;  // 16-byte segment: row e / kSeg
-                const int rr = e / kSeg, sg = e % kSeg;
-                const u32x4 v = *reinterpret_cast<const u32x4 *>(ot + rr * kOut + sg * 8);
-                if (m * 16 + rr < n_rows)
-                    store16(a.Y + (size_t)(row0 + m * 16 + rr) * ld + col0 + sg * 8, v);
+            for (int m = 0; m < kWMT; ++m) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = m * 16 + 4 * (ln >> 4) + i;
+                    if (m < n_mt && r < n_rows) {
+                        const size_t p = (size_t)(row0 + r);
+#pragma unroll
+                        for (int q = 0; q < kNTW / 2; ++q) {
+                            const size_t h_at = p * 2 * a.I + (2 * s64 + q) * 16 + c;
+                            a.H[h_at] = acc[m][2 * q][i];
+                            a.H[h_at + a.I] = acc[m][2 * q + 1][i];
+                        }
+                    }
+                }
             }
-            __builtin_amdgcn_wave_barrier();
+            continue;
+        }
+        constexpr int kOut = kGated ? kNTW / 2 * 16 : kNTW * 16;  // output columns: 32 or 64
+        constexpr int kSeg = kOut / 8;                            // 16-byte segments per row
+        uint16_t *ot = otile[g];
+        // this consumer's output columns start at column `col0` of the output rows
+        const int col0 = kGated ? 2 * s64 * 16 : s64 * 64;
+        const int ld = kGated ? a.I : a.n_canon;
+#pragma unroll
+        for (int m = 0; m < kWMT; ++m) {
+            if (m < n_mt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rr = 4 * (ln >> 4) + i;
+                    if (kGated) {
+#pragma unroll
+                        for (int q = 0; q < kNTW / 2; ++q) {
+                            float gate = acc[m][2 * q][i], up = acc[m][2 * q + 1][i];
+                            if (a.phase == 2 && m * 16 + rr < n_rows) {
+                                const size_t h_at =
+                                    (size_t)(row0 + m * 16 + rr) * 2 * a.I + (2 * s64 + q) * 16 + c;
+                                gate += a.H[h_at];
+                                up += a.H[h_at + a.I];
+                            }
+                            ot[rr * kOut + q * 16 + c] =
+                                (uint16_t)float_to_bf16_bits(silu_f32(gate) * up);
+                        }
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < kNTW; ++t)
+                            ot[rr * kOut + t * 16 + c] = (uint16_t)float_to_bf16_bits(acc[m][t][i]);
+                    }
+                }
+                // one wave: its LDS operations complete in order, so the reads
+                // below see every lane's writes above
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int h = 0; h < 16 * kSeg / kWave; ++h) {
+                    const int e = h * kWave + ln;  // 16-byte segment: row e / kSeg
+                    const int rr = e / kSeg, sg = e % kSeg;
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(ot + rr * kOut + sg * 8);
+                    if (m * 16 + rr < n_rows)
+                        store16(a.Y + (size_t)(row0 + m * 16 + rr) * ld + col0 + sg * 8, v);
+                }
+                __builtin_amdgcn_wave_barrier();
+            }
         }
     }
 }
@@ -367,9 +396,24 @@ bool gemm_wide_supported(int H, int I, int r_gu, int r_dn)
 
 int gemm_wide_slabs(int NT) { return (NT * 16 + kSlabCols - 1) / kSlabCols; }
 
-hipError_t launch_gemm_wide(const GemmArgs &a, bool gated, hipStream_t s)
+int gemm_wide_slabs_per_block(int n_slabs, int n_tiles, int E_l)
 {
-    const int blocks = gemm_grid_blocks(a.n_tiles, a.n_slabs);
+    // One block per CU.  When the work list holds about one tile per expert
+    // (the usual case, see gemm_tile_rows), a block takes enough adjacent
+    // slabs of its tile that the items fill the CUs about once: then no
+    // block waits for a second round, and a block's producers stream its
+    // next slab while its consumers still write the previous one.
+    const int tiles = std::max(1, std::min(n_tiles, E_l));
+    const int groups = std::max(1, std::min(n_slabs, (kWideCUs + tiles / 2) / tiles));
+    return (n_slabs + groups - 1) / groups;
+}
+
+hipError_t launch_gemm_wide(const GemmArgs &a_in, bool gated, hipStream_t s)
+{
+    GemmArgs a = a_in;
+    a.slabs_per_block = gemm_wide_slabs_per_block(a.n_slabs, a.n_tiles, a.E_l);
+    const int n_groups = (a.n_slabs + a.slabs_per_block - 1) / a.slabs_per_block;
+    const int blocks = gemm_grid_blocks(a.n_tiles, n_groups);
     if (blocks <= 0)
         return hipSuccess;
     if (gated)

@@ -114,6 +114,7 @@ struct GemmArgs {
     int E_l, k, I;
     uint16_t *Y;              // gated: act [n, I]; else y [n, n_canon]
     int n_slabs;
+    int slabs_per_block;      // wide kernel: adjacent slabs one block runs in turn (set by its launcher)
     const uint16_t *zeros;    // kZeroBytes of zeros
     int lb_shared;            // LB holds one stack per adapter ([L, 1, n_canon, r])
     // Split gate_up (the two-stream schedule): phase 1 runs the main K only
@@ -133,6 +134,7 @@ constexpr int kWideMaxTileRows = 176;
 // r_gu, r_dn: ranks of the active LoRA projections (0 when inactive)
 bool gemm_wide_supported(int H, int I, int r_gu, int r_dn);
 int gemm_wide_slabs(int NT);  // column slabs of the wide kernel for NT 16-column tiles
+int gemm_wide_slabs_per_block(int n_slabs, int n_tiles, int E_l);
 int gemm_tile_rows(int n_slots, int E_l, int H, int I, int r_gu, int r_dn);
 hipError_t launch_gemm_wide(const GemmArgs &a, bool gated, hipStream_t s);
 

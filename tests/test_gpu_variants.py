@@ -28,7 +28,7 @@ from mixture_experts_layer_up_amd import binding
 from mixture_experts_layer_up_amd.synth import CONFIGS, make_inputs
 from oracle import oracle
 from tests._gpu import SideStream, announce, bf16_to_np, cached_inputs, run_forward, tol
-from tests.test_gpu_forward import MID, MID_EP, WIDE
+from tests.test_gpu_forward import MID, MID_EP, SLAB_GROUPS, WIDE
 
 pytestmark = pytest.mark.gpu
 
@@ -136,7 +136,7 @@ def test_external_finalize_small_shapes():
         assert np.abs(y[e2p[local]] - ref_y[local]).max() <= tol(ref_y[local])
 
 
-@pytest.mark.parametrize("cfg", [MID, WIDE, SHARED_MID_EP], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [MID, WIDE, SHARED_MID_EP, SLAB_GROUPS], ids=lambda c: c.name)
 def test_two_stream_small_shapes_and_delta(cfg):
     announce(f"forward two-stream {cfg.name}")
     inp = make_inputs(cfg)

@@ -41,6 +41,14 @@ __device__ __forceinline__ void store16(void *p, u32x4 v)
     *reinterpret_cast<u32x4 *>(p) = v;
 }
 
+// Streaming store for large outputs that the next kernel reads once: the
+// nontemporal hint keeps tens of MB of dirty lines out of the caches, whose
+// later write-back would otherwise compete with the next weight streams.
+__device__ __forceinline__ void store16_stream(void *p, u32x4 v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v)
 {
     return __builtin_bit_cast(bf16x8, v);

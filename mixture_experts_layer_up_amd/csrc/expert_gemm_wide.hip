@@ -378,8 +378,8 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
                     const int e = h * kWave + ln;  // 16-byte segment: row e / kSeg
                     const int rr = e / kSeg, sg = e % kSeg;
                     const u32x4 v = *reinterpret_cast<const u32x4 *>(ot + rr * kOut + sg * 8);
-                    if (m * 16 + rr < n_rows)
-                        store16(a.Y + (size_t)(row0 + m * 16 + rr) * ld + col0 + sg * 8, v);
+                    if (m * 16 + rr < n_rows)  // tens of MB per launch: streaming store
+                        store16_stream(a.Y + (size_t)(row0 + m * 16 + rr) * ld + col0 + sg * 8, v);
                 }
                 __builtin_amdgcn_wave_barrier();
             }

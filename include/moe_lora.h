@@ -55,7 +55,10 @@ extern "C" {
 
 /* Number of events moe_lora_forward records when moe_lora_inputs.stage_events
  * is set: before routing, then after each of routing+permute, gate_up LoRA
- * shrink, gate_up GEMM (+SwiGLU), down LoRA shrink, down GEMM, finalize. */
+ * shrink, gate_up GEMM (+SwiGLU), down LoRA shrink, down GEMM, finalize.
+ * With at most 1024 slots (T * k) on one stream the gate_up shrink runs in
+ * the permute's launch, so its stage is empty (the third event follows the
+ * second directly). */
 #define MOE_LORA_NUM_STAGE_EVENTS 7
 
 /*

@@ -155,6 +155,33 @@ def test_no_adapter_paths_equal_base_bitwise():
     _compare(cfg.replace(num_loras=0), inp, base)
 
 
+@pytest.mark.parametrize("cfg", [
+    MID_EP,
+    SPLIT_FEW.replace(name="split_few_ep", local_expert_offset=32, local_num_experts=32, seed=45),
+    SLAB_GROUPS.replace(name="slab_groups_ep", local_expert_offset=64, local_num_experts=64,
+                        seed=46)], ids=lambda c: c.name)
+def test_no_local_slots(cfg):
+    """Every slot belongs to another expert-parallel shard: no permuted row,
+    no (adapter, expert) segment, no GEMM work item, and an all-zero output.
+    The three cases take the permute fused with the gate_up shrink, the
+    separate few-row launches, and the many-row kernels."""
+    announce(f"forward: no local slots {cfg.name}")
+    inp = make_inputs(cfg)
+    rng = np.random.default_rng(7)
+    T, k = cfg.num_tokens, cfg.top_k
+    ids = np.stack([rng.choice(cfg.local_expert_offset, k, replace=False)
+                    for _ in range(T)]).astype(np.int32)
+    w = np.full((T, k), 1.0 / k, np.float32)
+    got, r = run_forward(cfg, inp, use_logits=False, topk=(ids, w), routing=True)
+    assert np.all(got == 0)
+    assert np.all(r["expert_counts"] == 0) and np.all(r["expert_offsets"] == 0)
+    assert np.all(r["expanded_idx_to_permuted_idx"] == -1)
+    assert np.all(r["permuted_idx_to_expanded_idx"] == -1)
+    assert np.all(r["lora_seg_offsets"] == 0) and np.all(r["lora_seg_slots"] == -1)
+    ref = oracle.forward(cfg, inp, topk_ids=ids, topk_weights=w.astype(np.float64))
+    assert np.all(ref == 0)
+
+
 def test_topk_passthrough_with_invalid_slots():
     announce("forward: top-k passthrough")
     cfg = MID

@@ -161,9 +161,8 @@ int enqueue_routing(const moe_lora_shape *s, const float *logits, const float *b
     pa.E = s->num_experts;
     pa.flags = flags;
     // the gate_up shrink joins the permute's launch when the shapes allow it
-    if (fuse_shrink && permute_shrink_fusable(pa, *fuse_shrink)) {
-        ShrinkArgs sa = *fuse_shrink;
-        MOE_TRY(check(launch_permute_shrink(pa, sa, st)));
+    if (fuse_shrink && shrink_done && permute_shrink_fusable(pa, *fuse_shrink)) {
+        MOE_TRY(check(launch_permute_shrink(pa, *fuse_shrink, st)));
         *shrink_done = true;
         return MOE_LORA_OK;
     }
@@ -397,7 +396,7 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
                             gu && !two_stream ? &sa_gu : nullptr, &shrink_done));
     MOE_TRY(record(ev, 1, st));
 
-    if (gu && !shrink_done) {
+    if (gu && !shrink_done) {  // a launch of its own (many slots, or the side stream)
         const ShrinkArgs &sa = sa_gu;
         if (two_stream) {
             MOE_TRY(check(hipEventRecord(fork, st)));

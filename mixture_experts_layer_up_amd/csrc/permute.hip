@@ -22,7 +22,9 @@
 // position = offset of the key + slots of the key in earlier blocks + in
 // earlier waves of the block + in earlier 64-slot groups of the wave + lower
 // lanes of the group with the same key.  With G == 1 the rank kernel's own
-// histogram is the whole one and the count kernel is skipped.
+// histogram is the whole one and the count kernel is skipped, and in the
+// forward pass the rank pass shares its launch with the gate_up LoRA shrink
+// (permute_shrink_kernel, below).
 #include "device_common.h"
 #include "kernels.h"
 #include "lora_shrink_rows.h"

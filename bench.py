@@ -266,8 +266,20 @@ def traffic_from_profile(workload: str):
     return int(b.group(1))
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, inp, min_seconds: float):
-    """Time the CPU oracle (as is) on a bounded sample of the same workload."""
+    """Time the CPU oracle (as is) on a bounded sample of the same workload,
+    on all of the host's threads and on one."""
     import numpy as np
     from oracle import oracle
     T = cfg.num_tokens
@@ -275,18 +287,34 @@ def cpu_baseline(cfg, inp, min_seconds: float):
     toks = np.linspace(0, T - 1, n_tok).astype(np.int32) if n_tok < T else None
     ids, w = oracle.route(inp["logits"], cfg.top_k, bias=inp.get("routing_bias"),
                           method=getattr(cfg, "routing_method", 0))
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        oracle.forward(cfg, inp, topk_ids=ids, topk_weights=w, tokens=toks)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds:
-            break
+
+    def timed(seconds, tokens):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.forward(cfg, inp, topk_ids=ids, topk_weights=w, tokens=tokens)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return reps, el
+
+    threads = oracle.num_threads()
+    reps, el = timed(min_seconds, toks)
     sample = (f"{n_tok} of {T} tokens" + ("" if toks is None else " (evenly spaced)") +
               f" of the same seeded batch, routing precomputed, {reps} repetitions, {el:.1f} s")
-    return {"value": reps * n_tok / el, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "sample": sample}
+    # one thread, on a quarter of the sample (the per-token work is the same)
+    n1 = max(1, n_tok // 4)
+    toks1 = np.linspace(0, T - 1, n1).astype(np.int32)
+    oracle.set_num_threads(1)
+    try:
+        reps1, el1 = timed(min_seconds / 2, toks1)
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": reps * n_tok / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "cpu_model": _cpu_model(),
+            "single_core": {"value": reps1 * n1 / el1, "unit": "tokens/s",
+                            "sample": f"{n1} evenly spaced tokens, {reps1} repetitions, "
+                                      f"{el1:.1f} s, 1 thread"}}
 
 
 def main():

@@ -57,6 +57,17 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Threads for the following calls (timing only: results do not depend on it). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /*
  * Top-k routing.  For each token: the k experts with the largest selection
  * scores, ordered by (score descending, expert id ascending), where the

@@ -40,6 +40,8 @@ def _load():
         i32, f64 = ctypes.c_int, ctypes.c_double
         vp = ctypes.c_void_p
         lib.oracle_num_threads.restype = i32
+        lib.oracle_set_num_threads.argtypes = [i32]
+        lib.oracle_set_num_threads.restype = None
         lib.oracle_route.argtypes = [i32, i32, i32, vp, vp, i32, vp, vp]
         lib.oracle_route.restype = i32
         lib.oracle_permute.argtypes = [i32] * 6 + [vp] * 8
@@ -56,6 +58,11 @@ def _ptr(a: Optional[np.ndarray]):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the following oracle calls (results do not depend on it)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def route(logits: np.ndarray, top_k: int, bias: Optional[np.ndarray] = None, method: int = 0):

@@ -71,6 +71,12 @@ SPLIT_FEW = LayerConfig("split_few", 200, 256, 96, 64, 8, 0, 64, 4, 16, 16, seed
                         mapping="uniform", sigma_lora_a=0.2, sigma_lora_b=0.2)
 MANY_PAIRS = LayerConfig("many_pairs", 16, 128, 64, 17, 4, 0, 17, 64, 8, 8, seed=43,
                          mapping="uniform", sigma_lora_a=0.3, sigma_lora_b=0.3)
+# The fused launch's key tables at their limit: 8 adapters x 128 experts =
+# 1024 (adapter, expert) pairs, and 1024 local experts with one adapter.
+PAIRS_1024 = LayerConfig("pairs_1024", 16, 128, 64, 128, 8, 0, 128, 8, 8, 8, seed=47,
+                         mapping="uniform", sigma_lora_a=0.3, sigma_lora_b=0.3)
+EXPERTS_1024 = LayerConfig("experts_1024", 8, 128, 64, 1024, 8, 0, 1024, 1, 8, 8, seed=48,
+                           mapping="zero", sigma_lora_a=0.3, sigma_lora_b=0.3)
 # The many-row GEMM with several column slabs per block: 128 experts of ~40
 # rows (80-row tiles, about one per expert), so each block takes 2 of the 3
 # slabs of gate_up (2I = 640) and of down (H = 640): the second slab group
@@ -114,7 +120,8 @@ def test_prefill_sampled_tokens():
 
 @pytest.mark.parametrize("cfg", [MID, MID_R64, MID_EP, BIG_ROWS, TINY_AMP, WIDE, WIDE_R8,
                                  WIDE_H128, SHRINK_R20, SHRINK_MT2, SHRINK_FEW2, SHRINK_FEW3,
-                                 FUSED_FULL, SPLIT_FEW, MANY_PAIRS, SLAB_GROUPS],
+                                 FUSED_FULL, SPLIT_FEW, MANY_PAIRS, SLAB_GROUPS, PAIRS_1024,
+                                 EXPERTS_1024],
                          ids=lambda c: c.name)
 def test_small_shapes_and_lora_delta(cfg):
     announce(f"forward {cfg.name}")

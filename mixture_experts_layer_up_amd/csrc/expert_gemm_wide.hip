@@ -8,7 +8,7 @@
 //
 // Design for gfx950 when rows per expert are many:
 //  * One block = 8 waves = one (row tile of at most 176 rows of one expert,
-//    256-column slab), one block per CU.  Waves 0-3 are consumers: consumer
+//    256-column slab at a time), one block per CU.  Waves 0-3 are consumers: consumer
 //    w owns the slab's 64-column group w (for gate_up two gate/up pairs) for
 //    all 176 rows, and only reads LDS and issues MFMAs.  Waves 4-7 are
 //    producers: they only compute addresses and issue the direct
@@ -30,6 +30,13 @@
 //    zero block in the workspace instead (a direct load cannot mask).  An M
 //    tile (16 rows) skips the MFMAs of a chunk whose adapters it does not
 //    contain.  Needs rank % 8 == 0 (16-byte expand rows).
+//  * A block runs several adjacent slabs of its row tile in turn (slab
+//    groups, sized by the launcher so that the items fill the CUs about
+//    once).  The rows, and so the loads per chunk, are the same for every
+//    slab, so the producers run on into the next slab's chunks while the
+//    consumers write the previous slab's outputs.
+//  * Outputs (act, y: tens of MB) leave through a small per-consumer LDS
+//    tile as 16-byte streaming stores.
 //  * MFMA guards are scalar (wave-uniform) branches: MFMA ignores EXEC.
 #include <algorithm>
 #include <type_traits>

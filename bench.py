@@ -317,12 +317,244 @@ def cpu_baseline(cfg, inp, min_seconds: float):
                                       f"{el1:.1f} s, 1 thread"}}
 
 
+def measure(args, workload: str, steps: int, warmup: int, cold_steps: int, graph: bool,
+            two_stream: bool, finalize: str = "fused", lora_layout: str = "per_expert",
+            routing_method: int = 0, routing_bias_sigma: float = 0.0, cpu_seconds: float = 0.0,
+            copy_probe_mib: int = 0):
+    """Time one workload; returns its result fields (value, roofline, layer, ...)."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_up_amd import binding
+    from mixture_experts_layer_up_amd.synth import CONFIGS, make_inputs
+
+    cfg = CONFIGS[workload]
+    if lora_layout == "shared_outer":
+        cfg = cfg.replace(lora_shared_outer=True)
+    if routing_method or routing_bias_sigma > 0:
+        cfg = cfg.replace(routing_method=routing_method, routing_bias_sigma=routing_bias_sigma)
+    log(f"[bench] generating {workload} inputs")
+    inp = make_inputs(cfg)
+    torch.cuda.set_device(0)
+    shape, lay = binding.layer_from_host(cfg, inp)
+    ws = torch.empty(binding.workspace_size(shape), dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    kw = {k: v for k, v in lay.items() if k not in ("hidden", "w13_packed", "w2_packed")}
+
+    hip = HipEvents()
+    side_events = []
+    if two_stream:
+        side_stream = torch.cuda.Stream()   # default priority
+        side_events = hip.create(2, disable_timing=True)
+        kw.update(side_stream=side_stream.cuda_stream, fork_event=side_events[0],
+                  join_event=side_events[1])
+    ext_routing = binding.alloc_routing(shape, "cuda") if finalize == "external" else None
+    expert_out = (torch.empty((cfg.num_tokens * cfg.top_k, cfg.hidden), dtype=torch.bfloat16,
+                              device="cuda") if ext_routing is not None else None)
+
+    def step(events=None):
+        if ext_routing is None:
+            binding.forward(shape, lay["hidden"], lay["w13_packed"], lay["w2_packed"], out=out,
+                            workspace=ws, stage_events=events, **kw)
+        else:
+            binding.forward(shape, lay["hidden"], lay["w13_packed"], lay["w2_packed"],
+                            workspace=ws, stage_events=events, routing=ext_routing,
+                            expert_out=expert_out, **kw)
+            binding.finalize(shape, expert_out, ext_routing, out=out)
+
+    if copy_probe_mib > 0:
+        n = copy_probe_mib * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: read {copy_probe_mib} MiB, wrote {copy_probe_mib} MiB")
+        del src, dst
+
+    log(f"[bench] {workload}: warmup {warmup}")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = steps
+    nstage = len(binding.STAGE_NAMES)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    # The timed region: K steps launched from the host.  Every EVENT_EVERY-th
+    # step records the two stage events around the dominant kernel (the
+    # gate_up GEMM), whose elapsed time is that kernel's live duration; every
+    # recorded event costs stream time (two cost ~5 us), so the other
+    # boundaries are left out and the sampled steps are spread evenly.
+    gi = binding.STAGE_NAMES.index("gemm_gate_up_swiglu")  # between events gi, gi + 1
+    kev = [hip.create(2) for _ in range((K + EVENT_EVERY - 1) // EVENT_EVERY)]
+
+    def dominant_events(pair):
+        ev = [None] * binding.NUM_STAGE_EVENTS
+        ev[gi], ev[gi + 1] = pair
+        return ev
+
+    plan = [dominant_events(kev[s_ // EVENT_EVERY]) if s_ % EVENT_EVERY == 0 else None
+            for s_ in range(K)]
+    start, end = hip.create(2)
+    log(f"[bench] {workload}: timing {K} steps")
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    hip.record(start, stream)
+    for s_ in range(K):
+        step(plan[s_])
+    hip.record(end, stream)
+    hip.sync(end)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    ms_per_step = hip.elapsed_ms(start, end) / K
+    gate_up_ms = sum(hip.elapsed_ms(a, b) for a, b in kev) / len(kev)
+    for p in kev:
+        hip.destroy(p)
+    hip.destroy([start, end])
+
+    # Stage breakdown (diagnostic, outside the timed region): steps with all
+    # seven stage events recorded.
+    KB = min(K, 50)
+    evs = [hip.create(binding.NUM_STAGE_EVENTS) for _ in range(KB)]
+    for s_ in range(KB):
+        step(evs[s_])
+    torch.cuda.synchronize()
+    stage_ms = np.zeros(nstage)
+    for s_ in range(KB):
+        for i in range(nstage):
+            stage_ms[i] += hip.elapsed_ms(evs[s_][i], evs[s_][i + 1])
+    stage_ms /= KB
+    for e in evs:
+        hip.destroy(e)
+
+    # the same K steps captured into one HIP graph and replayed (the forward
+    # allocates nothing and never waits on the host); reported beside `value`
+    graph_ms = None
+    if graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(K):
+                step()
+        g.replay()
+        torch.cuda.synchronize()
+        gs, ge = hip.create(2)
+        hip.record(gs, stream)
+        g.replay()
+        hip.record(ge, stream)
+        hip.sync(ge)
+        graph_ms = hip.elapsed_ms(gs, ge) / K
+        hip.destroy([gs, ge])
+        del g
+        log(f"[bench] {workload}: graph replay {graph_ms * 1e3:.1f} us/step")
+
+    # Cold cache (diagnostic, outside the timed region): before each of KC
+    # steps a 512 MiB buffer is rewritten, so the 256 MiB Infinity Cache
+    # holds none of the layer's data; each step is timed alone between two
+    # events.  Back-to-back steps (the timed region) keep only what the
+    # previous step left in that cache.
+    cold = None
+    if cold_steps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cev = [hip.create(2) for _ in range(cold_steps)]
+        for s_, (a_, b_) in enumerate(cev):
+            flush.fill_(s_ & 0xff)
+            hip.record(a_, stream)
+            step()
+            hip.record(b_, stream)
+        torch.cuda.synchronize()
+        cms = np.array([hip.elapsed_ms(a_, b_) for a_, b_ in cev])
+        for e in cev:
+            hip.destroy(e)
+        del flush
+        cold = {"steps": cold_steps, "ms_median": float(np.median(cms)),
+                "ms_p90": float(np.percentile(cms, 90)), "ms_min": float(cms.min()),
+                "tokens_per_s_median": cfg.num_tokens / (float(np.median(cms)) / 1e3)}
+        log(f"[bench] {workload}: cold cache median {cold['ms_median'] * 1e3:.1f} us/step")
+
+    # the cost model counts what this batch's routing touches (the library's own routing)
+    routing = binding.alloc_routing(shape, "cuda")
+    binding.forward(shape, lay["hidden"], lay["w13_packed"], lay["w2_packed"], out=out,
+                    workspace=ws, routing=routing, **kw)
+    torch.cuda.synchronize()
+    cost = algorithmic_cost(cfg, routing["topk_ids"].cpu().numpy(), inp["mapping"])
+    hip.destroy(side_events)
+    t_s = ms_per_step / 1e3
+    achieved = cost["gate_up_bytes"] / (gate_up_ms / 1e3) / 1e9
+    gate_up_tflops = cost["gate_up_flops"] / (gate_up_ms / 1e3) / 1e12
+    layer_gbps = cost["bytes"] / t_s / 1e9
+    layer_tflops = cost["flops"] / t_s / 1e12
+    # the layer's roofline time: the larger of its HBM and MFMA floors
+    floor_s = max(cost["bytes"] / (HBM_PEAK_GBPS * 1e9), cost["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+
+    cpu = None
+    if cpu_seconds > 0:
+        log("[bench] CPU oracle baseline")
+        cpu = cpu_baseline(cfg, inp, cpu_seconds)
+
+    return {
+        "cfg": cfg,
+        "value": cfg.num_tokens / t_s,
+        "ms_per_step": ms_per_step,
+        "config": {"workload": f"{workload}: {WORKLOAD_TEXT[workload]}",
+                   "num_tokens": cfg.num_tokens, "hidden": cfg.hidden, "inter": cfg.inter,
+                   "num_experts": cfg.num_experts, "top_k": cfg.top_k,
+                   "local_expert_offset": cfg.local_expert_offset,
+                   "local_num_experts": cfg.local_num_experts, "num_loras": cfg.num_loras,
+                   "rank": cfg.rank_gate_up, "lora_layout": lora_layout,
+                   "finalize": finalize, "two_stream": bool(two_stream),
+                   "routing_method": routing_method,
+                   "routing_bias_sigma": routing_bias_sigma,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "gemm_gate_up_swiglu",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic_from_profile(workload),
+                     "algorithmic_bytes_per_launch": cost["gate_up_bytes"],
+                     "algorithmic_flops_per_launch": cost["gate_up_flops"],
+                     "mfma_tflops": gate_up_tflops,
+                     "mfma_frac": gate_up_tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "kernel_us": gate_up_ms * 1e3},
+        "layer": {"algorithmic_bytes": cost["bytes"], "flops": cost["flops"],
+                  "hbm_gbps": layer_gbps, "hbm_frac": layer_gbps / HBM_PEAK_GBPS,
+                  "mfma_tflops": layer_tflops, "mfma_frac": layer_tflops / MFMA_BF16_PEAK_TFLOPS,
+                  "roofline_us": floor_s * 1e6, "roofline_frac": floor_s / t_s,
+                  "mfma_frac_at_hbm_peak": cost["flops"] / floor_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                  "touched_experts": cost["touched_experts"],
+                  "touched_lora_pairs": cost["touched_lora_pairs"],
+                  "local_slots": cost["local_slots"]},
+        "stages_us": {n: float(v * 1e3) for n, v in zip(binding.STAGE_NAMES, stage_ms)},
+        "wall_ms_per_step": wall_s * 1e3 / K,
+        "graph_replay": None if graph_ms is None else {
+            "ms_per_step": graph_ms, "tokens_per_s": cfg.num_tokens / (graph_ms / 1e3),
+            "layer_hbm_frac": cost["bytes"] / (graph_ms / 1e3) / 1e9 / HBM_PEAK_GBPS},
+        "cold_cache": None if cold is None else {
+            **cold, "layer_hbm_frac": cost["bytes"] / (cold["ms_median"] / 1e3) / 1e9 / HBM_PEAK_GBPS},
+        "cpu_baseline": cpu,
+    }
+
+
+TIMING_TEXT = ("K host-launched steps between two HIP events on the launch stream; in every "
+               f"{EVENT_EVERY}th step two more events bracket the gate_up GEMM (roofline "
+               "kernel_us, the mean over those launches); stages_us comes from a separate "
+               "pass with all seven stage events")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode64", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--prefill-leg", type=int, default=1,
+                    help="with the default decode64 workload, also time the T=2048 prefill "
+                         "layer and report it under `prefill` (1 = yes)")
+    ap.add_argument("--prefill-steps", type=int, default=50)
     ap.add_argument("--lora-layout", default="per_expert", choices=("per_expert", "shared_outer"),
                     help="LoRA stack layout (shared_outer: A_gu and B_dn one set per adapter)")
     ap.add_argument("--finalize", default="fused", choices=("fused", "external"),
@@ -333,8 +565,8 @@ def main():
     ap.add_argument("--routing-bias-sigma", type=float, default=0.0,
                     help="> 0: a per-expert selection bias drawn N(0, sigma)")
     ap.add_argument("--two-stream", type=int, default=0,
-                    help="1: gate_up LoRA shrink on a second stream, concurrent with the "
-                         "main-K part of the gate_up GEMM")
+                    help="1: gate_up LoRA shrink on a second stream beside the permute "
+                         "(decode-shaped batches)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle baseline time budget (0 = skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -370,225 +602,46 @@ def main():
               "(multi-GPU expert parallelism is a design note only)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
-    import torch
-
-    from mixture_experts_layer_up_amd import binding
-    from mixture_experts_layer_up_amd.synth import CONFIGS, make_inputs
-
-    cfg = CONFIGS[args.workload]
-    if args.lora_layout == "shared_outer":
-        cfg = cfg.replace(lora_shared_outer=True)
-    if args.routing_method or args.routing_bias_sigma > 0:
-        cfg = cfg.replace(routing_method=args.routing_method,
-                          routing_bias_sigma=args.routing_bias_sigma)
-    log(f"[bench] generating {args.workload} inputs")
-    inp = make_inputs(cfg)
-    torch.cuda.set_device(0)
-    shape, lay = binding.layer_from_host(cfg, inp)
-    ws = torch.empty(binding.workspace_size(shape), dtype=torch.uint8, device="cuda")
-    out = torch.empty((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
-    kw = {k: v for k, v in lay.items() if k not in ("hidden", "w13_packed", "w2_packed")}
-
-    if args.two_stream:
-        side_stream = torch.cuda.Stream()   # default priority
-        hip_side = HipEvents()
-        fork_ev, join_ev = hip_side.create(2, disable_timing=True)
-        kw.update(side_stream=side_stream.cuda_stream, fork_event=fork_ev, join_event=join_ev)
-    ext_routing = binding.alloc_routing(shape, "cuda") if args.finalize == "external" else None
-    expert_out = (torch.empty((cfg.num_tokens * cfg.top_k, cfg.hidden), dtype=torch.bfloat16,
-                              device="cuda") if ext_routing is not None else None)
-
-    def step(events=None):
-        if ext_routing is None:
-            binding.forward(shape, lay["hidden"], lay["w13_packed"], lay["w2_packed"], out=out,
-                            workspace=ws, stage_events=events, **kw)
-        else:
-            binding.forward(shape, lay["hidden"], lay["w13_packed"], lay["w2_packed"],
-                            workspace=ws, stage_events=events, routing=ext_routing,
-                            expert_out=expert_out, **kw)
-            binding.finalize(shape, expert_out, ext_routing, out=out)
-
-    if args.copy_probe_mib > 0:
-        n = args.copy_probe_mib * (1 << 20) // 2
-        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
-        dst = torch.empty_like(src)
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        log(f"[bench] copy probe: read {args.copy_probe_mib} MiB, wrote {args.copy_probe_mib} MiB")
-        del src, dst
-
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    hip = HipEvents()
-    K = args.steps
-    nstage = len(binding.STAGE_NAMES)
-    stream = torch.cuda.current_stream().cuda_stream
-
-    # The timed region: K steps launched from the host.  Every EVENT_EVERY-th
-    # step records the two stage events around the dominant kernel (the
-    # gate_up GEMM), whose elapsed time is that kernel's live duration; every
-    # recorded event costs stream time (two cost ~5 us), so the other
-    # boundaries are left out and the sampled steps are spread evenly.
-    gi = binding.STAGE_NAMES.index("gemm_gate_up_swiglu")  # between events gi, gi + 1
-    kev = [hip.create(2) for _ in range((K + EVENT_EVERY - 1) // EVENT_EVERY)]
-
-    def dominant_events(pair):
-        ev = [None] * binding.NUM_STAGE_EVENTS
-        ev[gi], ev[gi + 1] = pair
-        return ev
-
-    plan = [dominant_events(kev[s_ // EVENT_EVERY]) if s_ % EVENT_EVERY == 0 else None
-            for s_ in range(K)]
-    start, end = hip.create(2)
-    log(f"[bench] timing {K} steps")
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    hip.record(start, stream)
-    for s_ in range(K):
-        step(plan[s_])
-    hip.record(end, stream)
-    hip.sync(end)
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t_wall
-    ms_per_step = hip.elapsed_ms(start, end) / K
-    gate_up_ms = sum(hip.elapsed_ms(a, b) for a, b in kev) / len(kev)
-    for p in kev:
-        hip.destroy(p)
-    hip.destroy([start, end])
-
-    # Stage breakdown (diagnostic, outside the timed region): steps with all
-    # seven stage events recorded.
-    KB = min(K, 50)
-    evs = [hip.create(binding.NUM_STAGE_EVENTS) for _ in range(KB)]
-    for s_ in range(KB):
-        step(evs[s_])
-    torch.cuda.synchronize()
-    stage_ms = np.zeros(nstage)
-    for s_ in range(KB):
-        for i in range(nstage):
-            stage_ms[i] += hip.elapsed_ms(evs[s_][i], evs[s_][i + 1])
-    stage_ms /= KB
-    for e in evs:
-        hip.destroy(e)
-
-    # the same K steps captured into one HIP graph and replayed (the forward
-    # allocates nothing and never waits on the host); reported beside `value`
-    graph_ms = None
-    if args.graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(K):
-                step()
-        g.replay()
-        torch.cuda.synchronize()
-        gs, ge = hip.create(2)
-        hip.record(gs, stream)
-        g.replay()
-        hip.record(ge, stream)
-        hip.sync(ge)
-        graph_ms = hip.elapsed_ms(gs, ge) / K
-        hip.destroy([gs, ge])
-        del g
-        log(f"[bench] graph replay: {graph_ms * 1e3:.1f} us/step")
-
-    # Cold cache (diagnostic, outside the timed region): before each of KC
-    # steps a 512 MiB buffer is rewritten, so the 256 MiB Infinity Cache
-    # holds none of the layer's data; each step is timed alone between two
-    # events.  Back-to-back steps (the timed region) keep only what the
-    # previous step left in that cache.
-    cold = None
-    if args.cold_steps > 0:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        cev = [hip.create(2) for _ in range(args.cold_steps)]
-        for s_, (a_, b_) in enumerate(cev):
-            flush.fill_(s_ & 0xff)
-            hip.record(a_, stream)
-            step()
-            hip.record(b_, stream)
-        torch.cuda.synchronize()
-        cms = np.array([hip.elapsed_ms(a_, b_) for a_, b_ in cev])
-        for e in cev:
-            hip.destroy(e)
-        del flush
-        cold = {"steps": args.cold_steps, "ms_median": float(np.median(cms)),
-                "ms_p90": float(np.percentile(cms, 90)), "ms_min": float(cms.min()),
-                "tokens_per_s_median": cfg.num_tokens / (float(np.median(cms)) / 1e3)}
-        log(f"[bench] cold cache: median {cold['ms_median'] * 1e3:.1f} us/step")
-
-    # the cost model counts what this batch's routing touches (the library's own routing)
-    routing = binding.alloc_routing(shape, "cuda")
-    binding.forward(shape, lay["hidden"], lay["w13_packed"], lay["w2_packed"], out=out,
-                    workspace=ws, routing=routing, **kw)
-    torch.cuda.synchronize()
-    cost = algorithmic_cost(cfg, routing["topk_ids"].cpu().numpy(), inp["mapping"])
-    t_s = ms_per_step / 1e3
-    achieved = cost["gate_up_bytes"] / (gate_up_ms / 1e3) / 1e9
-    layer_gbps = cost["bytes"] / t_s / 1e9
-    layer_tflops = cost["flops"] / t_s / 1e12
-
-    cpu = None
-    if args.cpu_seconds > 0:
-        log("[bench] CPU oracle baseline")
-        cpu = cpu_baseline(cfg, inp, args.cpu_seconds)
-
+    r = measure(args, args.workload, args.steps, args.warmup, args.cold_steps, bool(args.graph),
+                bool(args.two_stream), args.finalize, args.lora_layout, args.routing_method,
+                args.routing_bias_sigma, args.cpu_seconds, args.copy_probe_mib)
     result = {
         "metric": METRIC,
-        "value": cfg.num_tokens / t_s,
+        "value": r["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded numpy PCG64; random-init weights of the layer's shapes)",
-        "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}",
-                   "num_tokens": cfg.num_tokens, "hidden": cfg.hidden, "inter": cfg.inter,
-                   "num_experts": cfg.num_experts, "top_k": cfg.top_k,
-                   "local_expert_offset": cfg.local_expert_offset,
-                   "local_num_experts": cfg.local_num_experts, "num_loras": cfg.num_loras,
-                   "rank": cfg.rank_gate_up, "lora_layout": args.lora_layout,
-                   "finalize": args.finalize, "two_stream": bool(args.two_stream),
-                   "routing_method": args.routing_method,
-                   "routing_bias_sigma": args.routing_bias_sigma,
-                   "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "gemm_gate_up_swiglu",
-                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic_from_profile(args.workload),
-                     "algorithmic_bytes_per_launch": cost["gate_up_bytes"],
-                     "kernel_us": gate_up_ms * 1e3},
-        "layer": {"algorithmic_bytes": cost["bytes"], "flops": cost["flops"],
-                  "hbm_gbps": layer_gbps, "hbm_frac": layer_gbps / HBM_PEAK_GBPS,
-                  "mfma_tflops": layer_tflops, "mfma_frac": layer_tflops / MFMA_BF16_PEAK_TFLOPS,
-                  "touched_experts": cost["touched_experts"],
-                  "touched_lora_pairs": cost["touched_lora_pairs"],
-                  "local_slots": cost["local_slots"]},
-        "stages_us": {n: float(v * 1e3) for n, v in zip(binding.STAGE_NAMES, stage_ms)},
-        "timing": "K host-launched steps between two HIP events on the launch stream; in every "
-                  f"{EVENT_EVERY}th step two more events bracket the gate_up GEMM (roofline "
-                  "kernel_us, the mean over those launches); stages_us comes from a separate "
-                  "pass with all seven stage events",
-        "wall_ms_per_step": wall_s * 1e3 / K,
-        "graph_replay": None if graph_ms is None else {
-            "ms_per_step": graph_ms, "tokens_per_s": cfg.num_tokens / (graph_ms / 1e3),
-            "layer_hbm_frac": cost["bytes"] / (graph_ms / 1e3) / 1e9 / HBM_PEAK_GBPS},
-        "cold_cache": None if cold is None else {
-            **cold, "layer_hbm_frac": cost["bytes"] / (cold["ms_median"] / 1e3) / 1e9 / HBM_PEAK_GBPS},
-        "cpu_baseline": cpu,
+        "config": r["config"],
+        "roofline": r["roofline"],
+        "layer": r["layer"],
+        "stages_us": r["stages_us"],
+        "timing": TIMING_TEXT,
+        "wall_ms_per_step": r["wall_ms_per_step"],
+        "graph_replay": r["graph_replay"],
+        "cold_cache": r["cold_cache"],
+        "cpu_baseline": r["cpu_baseline"],
     }
+    # The metric's prefill half: the T=2048 layer, its dominant kernel against
+    # the HBM roofline (it sits below the MFMA ridge) and its MFMA fraction.
+    if args.workload == "decode64" and args.prefill_leg and args.lora_layout == "per_expert" \
+            and args.finalize == "fused" and not args.routing_method and not args.routing_bias_sigma:
+        import torch
+        torch.cuda.empty_cache()
+        p = measure(args, "prefill", args.prefill_steps, max(2, args.warmup // 4),
+                    min(args.cold_steps, 10), bool(args.graph), bool(args.two_stream))
+        result["prefill"] = {
+            "value": p["value"], "unit": "tokens/s", "steps": args.prefill_steps,
+            "ms_per_step": p["ms_per_step"], "config": p["config"], "roofline": p["roofline"],
+            "layer": p["layer"], "stages_us": p["stages_us"], "graph_replay": p["graph_replay"],
+            "cold_cache": p["cold_cache"],
+        }
     print(json.dumps(result))
 
 

@@ -57,8 +57,8 @@ extern "C" {
  * is set: before routing, then after each of routing+permute, gate_up LoRA
  * shrink, gate_up GEMM (+SwiGLU), down LoRA shrink, down GEMM, finalize.
  * With at most 1024 slots (T * k) on one stream the gate_up shrink runs in
- * the permute's launch, so its stage is empty (the third event follows the
- * second directly). */
+ * the permute's launch, and with a side stream it runs there, so its stage
+ * is then empty (the third event follows the second directly). */
 #define MOE_LORA_NUM_STAGE_EVENTS 7
 
 /*
@@ -187,14 +187,25 @@ typedef struct moe_lora_routing {
  *                      completes it.  Needs `routing`, which holds the other
  *                      two members of the triple.
  *   side_stream        NULL (everything on `stream`), or a second hipStream_t
- *                      (default priority) for the gate_up LoRA shrink, which
- *                      then runs concurrently with the main-K part of the
- *                      gate_up GEMM (the pages' two-stream schedule: "BF16
- *                      support for the experimental_sgl_trtllm MoE-LoRA
- *                      path", Summary (phase 2) and Flow section 1(B)).  The
- *                      GEMM is then split in two launches joined by an fp32
- *                      pre-activation in the workspace: results equal the
- *                      one-stream ones within rounding, not bitwise.
+ *                      (default priority, not `stream`) for the gate_up LoRA
+ *                      shrink, the pages' two-stream schedule ("BF16 support
+ *                      for the experimental_sgl_trtllm MoE-LoRA path",
+ *                      Summary (phase 2) and Flow section 1(B): the gate_up
+ *                      LoRA on a side stream, only for decode-sized batches,
+ *                      joined before the activation).  Used for decode-shaped
+ *                      batches only: num_tokens <= 256, num_tokens * top_k <=
+ *                      2048, and LoRA segments of fewer than 16 rows on
+ *                      average (num_tokens * top_k <= 15 * num_loras *
+ *                      local_num_experts) or a gate_up rank above 64;
+ *                      otherwise, and when the gate_up LoRA
+ *                      is inactive, it is ignored and everything runs on
+ *                      `stream`.  When used, the shrink runs on side_stream
+ *                      straight from the routing while `stream` runs the
+ *                      permute, and `stream` waits for it before the gate_up
+ *                      GEMM (which holds the LoRA expand and the
+ *                      activation).  The shrink computes every row exactly as
+ *                      the one-stream path does: the output is bitwise the
+ *                      one-stream output.
  *   input_flags        NULL, or one device int32 into which the MOE_LORA_FLAG_*
  *                      bits of this call are ORed (when NULL and `routing`
  *                      is given, routing->input_flags is used)
@@ -203,9 +214,9 @@ typedef struct moe_lora_routing {
  *                      recorded on `stream` after routing and waited by
  *                      side_stream; join_event is recorded on side_stream
  *                      after the shrink and waited by `stream` before the
- *                      LoRA expand.  Nothing is allocated, so a two-stream
- *                      forward can be captured into a HIP graph.  Ignored
- *                      when the gate_up LoRA is inactive.
+ *                      gate_up GEMM.  Nothing is allocated, so a two-stream
+ *                      forward can be captured into a HIP graph.  Not
+ *                      touched when side_stream is ignored (see above).
  * LoRA pointers may be NULL when the projection is inactive.
  */
 typedef struct moe_lora_inputs {
@@ -230,9 +241,8 @@ typedef struct moe_lora_inputs {
 } moe_lora_inputs;
 
 /* Bytes of device workspace moe_lora_forward needs for `shape` (host only,
- * pure; 0 for an invalid shape), including the fp32 pre-activation
- * [T*k, 2I] that the two-stream schedule uses.  The workspace must be
- * 256-byte aligned. */
+ * pure; 0 for an invalid shape), with or without a side stream.  The
+ * workspace must be 256-byte aligned. */
 size_t moe_lora_workspace_size(const moe_lora_shape *shape);
 
 /* Bytes of the packed expert weights (equal to the unpacked sizes). */

@@ -67,7 +67,7 @@ bool lora_down_active(const moe_lora_shape *s) { return s->num_loras > 0 && s->r
 // Workspace regions; every offset is a multiple of 256 bytes.
 struct Layout {
     size_t ids, weights, counts, offsets, exp2perm, perm2exp, seg_offsets, seg_slots;
-    size_t perm_scratch, tiles, tile_count, zeros, s_gu, act, s_dn, y, h;
+    size_t perm_scratch, tiles, tile_count, zeros, s_gu, act, s_dn, y;
     int tile_rows, max_tiles;
     size_t total;
 };
@@ -104,7 +104,6 @@ Layout make_layout(const moe_lora_shape *s)
     L.act = take(n * (size_t)s->inter * 2);
     L.s_dn = take(lora_down_active(s) ? n * round8(s->rank_down) * 2 : 0);
     L.y = take(n * (size_t)s->hidden * 2);
-    L.h = take(n * 2 * (size_t)s->inter * 4);  // two-stream schedule only
     L.total = o;
     return L;
 }
@@ -130,9 +129,10 @@ int enqueue_routing(const moe_lora_shape *s, const float *logits, const float *b
                     const RoutingPtrs &r, int32_t *block_counts, hipStream_t st,
                     int4 *tiles = nullptr, int tile_rows = 0, int max_tiles = 0,
                     int32_t *tile_count = nullptr, void *zeros = nullptr,
-                    const ShrinkArgs *fuse_shrink = nullptr, bool *shrink_done = nullptr)
+                    const ShrinkArgs *fuse_shrink = nullptr, bool *shrink_done = nullptr,
+                    bool routed = false)
 {
-    if (logits) {
+    if (logits && !routed) {
         RouteArgs ra{logits, r.ids, r.weights, s->num_tokens, s->num_experts, s->top_k,
                      bias, s->routing_method};
         MOE_TRY(check(launch_route(ra, st)));
@@ -307,6 +307,8 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
         return MOE_LORA_ERR_INVALID_ARG;
     if (in->side_stream && (!in->fork_event || !in->join_event))
         return MOE_LORA_ERR_INVALID_ARG;
+    if (in->side_stream && in->side_stream == stream)
+        return MOE_LORA_ERR_INVALID_ARG;
     const bool from_logits = in->router_logits != nullptr;
     if (from_logits == (in->topk_ids != nullptr || in->topk_weights != nullptr))
         return MOE_LORA_ERR_INVALID_ARG;
@@ -372,12 +374,6 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
                              : reinterpret_cast<uint16_t *>(ws + lay.y);
     const uint16_t *hidden = static_cast<const uint16_t *>(in->hidden);
 
-    // Two-stream schedule: the gate_up shrink runs on the side stream while
-    // the main-K part of the gate_up GEMM runs here; the expand waits for it.
-    const bool two_stream = gu && in->side_stream != nullptr;
-    hipStream_t side = static_cast<hipStream_t>(in->side_stream);
-    hipEvent_t fork = static_cast<hipEvent_t>(in->fork_event);
-    hipEvent_t join = static_cast<hipEvent_t>(in->join_event);
     const ShrinkArgs sa_gu{hidden, 1, H, static_cast<const uint16_t *>(in->lora_a_gate_up),
                            rg, round8(rg), L, E_l, k, r.seg_offsets, r.seg_slots, r.exp2perm,
                            s_gu, T * k, shape->lora_shared_outer};
@@ -387,26 +383,55 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     void *zeros = ws + lay.zeros;
     int32_t *tile_count = reinterpret_cast<int32_t *>(ws + lay.tile_count);
     int32_t *flags = in->input_flags ? in->input_flags : routing ? routing->input_flags : nullptr;
-    // one stream: the gate_up shrink may run in the permute's launch
-    bool shrink_done = false;
-    MOE_TRY(enqueue_routing(shape, in->router_logits, in->routing_bias, in->topk_ids,
-                            in->token_lora_mapping, flags, r,
-                            reinterpret_cast<int32_t *>(ws + lay.perm_scratch), st,
-                            tiles, lay.tile_rows, lay.max_tiles, tile_count, zeros,
-                            gu && !two_stream ? &sa_gu : nullptr, &shrink_done));
-    MOE_TRY(record(ev, 1, st));
+    int32_t *perm_scratch = reinterpret_cast<int32_t *>(ws + lay.perm_scratch);
 
-    if (gu && !shrink_done) {  // a launch of its own (many slots, or the side stream)
-        const ShrinkArgs &sa = sa_gu;
-        if (two_stream) {
-            MOE_TRY(check(hipEventRecord(fork, st)));
-            MOE_TRY(check(hipStreamWaitEvent(side, fork, 0)));
-            MOE_TRY(check(launch_shrink(sa, side)));
-            MOE_TRY(check(hipEventRecord(join, side)));
-        } else {
-            MOE_TRY(check(launch_shrink(sa, st)));
+    // Two-stream schedule (decode-shaped batches only): after routing, the
+    // gate_up shrink runs on the side stream, straight from the ids and the
+    // adapter mapping, while this stream runs the permute; this stream waits
+    // for it before the gate_up GEMM, whose expand reads its output.  The
+    // shrink computes every row as the one-stream launches do, so the result
+    // is bitwise the one-stream result.
+    PermuteArgs side_pa{};
+    side_pa.topk_ids = from_logits ? r.ids : in->topk_ids;
+    side_pa.mapping = in->token_lora_mapping;
+    side_pa.T = T;
+    side_pa.k = k;
+    side_pa.off = shape->local_expert_offset;
+    side_pa.E_l = E_l;
+    side_pa.L = L;
+    const bool two_stream = gu && in->side_stream != nullptr && T <= kTwoStreamMaxTokens &&
+                            shrink_by_ids_supported(side_pa, sa_gu);
+    bool shrink_done = false;
+    if (two_stream) {
+        hipStream_t side = static_cast<hipStream_t>(in->side_stream);
+        hipEvent_t fork = static_cast<hipEvent_t>(in->fork_event);
+        hipEvent_t join = static_cast<hipEvent_t>(in->join_event);
+        if (from_logits) {
+            RouteArgs ra{in->router_logits, r.ids, r.weights, T, shape->num_experts, k,
+                         in->routing_bias, shape->routing_method};
+            MOE_TRY(check(launch_route(ra, st)));
         }
+        MOE_TRY(check(hipEventRecord(fork, st)));
+        MOE_TRY(check(hipStreamWaitEvent(side, fork, 0)));
+        MOE_TRY(check(launch_shrink_by_ids(side_pa, sa_gu, side)));
+        MOE_TRY(check(hipEventRecord(join, side)));
+        MOE_TRY(enqueue_routing(shape, in->router_logits, in->routing_bias, in->topk_ids,
+                                in->token_lora_mapping, flags, r, perm_scratch, st, tiles,
+                                lay.tile_rows, lay.max_tiles, tile_count, zeros, nullptr,
+                                nullptr, /*routed=*/true));
+        MOE_TRY(record(ev, 1, st));
+        MOE_TRY(check(hipStreamWaitEvent(st, join, 0)));
+        shrink_done = true;
+    } else {
+        // one stream: the gate_up shrink may run in the permute's launch
+        MOE_TRY(enqueue_routing(shape, in->router_logits, in->routing_bias, in->topk_ids,
+                                in->token_lora_mapping, flags, r, perm_scratch, st, tiles,
+                                lay.tile_rows, lay.max_tiles, tile_count, zeros,
+                                gu ? &sa_gu : nullptr, &shrink_done));
+        MOE_TRY(record(ev, 1, st));
     }
+    if (gu && !shrink_done)  // a launch of its own (many slots)
+        MOE_TRY(check(launch_shrink(sa_gu, st)));
     MOE_TRY(record(ev, 2, st));
 
     GemmArgs g1{};
@@ -437,16 +462,7 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     };
     g1.n_slabs = slabs(g1.NT);
     g1.zeros = static_cast<const uint16_t *>(zeros);
-    if (two_stream) {
-        g1.H = reinterpret_cast<float *>(ws + lay.h);
-        g1.phase = 1;
-        MOE_TRY(check(launch_gemm_gate_up(g1, st)));
-        MOE_TRY(check(hipStreamWaitEvent(st, join, 0)));
-        g1.phase = 2;
-        MOE_TRY(check(launch_gemm_gate_up(g1, st)));
-    } else {
-        MOE_TRY(check(launch_gemm_gate_up(g1, st)));
-    }
+    MOE_TRY(check(launch_gemm_gate_up(g1, st)));
     MOE_TRY(record(ev, 3, st));
 
     if (dn) {

@@ -39,6 +39,7 @@
 #include <cmath>
 
 #include "device_common.h"
+#include "gemm_index.h"
 #include "kernels.h"
 #include "lora_shrink_rows.h"
 #include "mfma_pipeline.h"
@@ -86,47 +87,37 @@ __global__ __launch_bounds__(256, MT == 1 ? (kRank8 ? MOE_LORA_DECODE_WAVES : 3)
     // waves take K chunks round-robin (wave w: chunks w, w + 4, ...), so the
     // block's loads at any moment cover one contiguous stretch of its slab
     const int KC = a.K >> 5;
-    // this wave's main chunks (none in phase 2)
-    const int nm = (a.phase != 2 && wave < KC) ? (KC - wave + 3) >> 2 : 0;
-    const bool lora = a.S != nullptr && a.L > 0 && a.r > 0 && a.phase != 1;
+    const int nm = decode_main_chunks(KC, wave);  // this wave's main chunks
+    const bool lora = a.S != nullptr && a.L > 0 && a.r > 0;
     const int n_ext = lora ? (a.L * a.rp + 31) >> 5 : 0;
     const int ne = wave < n_ext ? (n_ext - wave + 3) >> 2 : 0;  // ext chunks wave, wave+4, ..
     const int nv = nm + ne;
 
-    // this block's slab: KC chunks of NS consecutive 1 KiB fragments
-    const uint16_t *wbase =
-        a.Wp + ((size_t)le * a.n_slabs + slab) * (size_t)KC * NS * 512 + lane * 8;
-    // Branch-free loaders: the address is selected (always a valid one) and
-    // the value masked, so every chunk issues the same loads.
+    // Branch-free loaders: every chunk issues the same loads, at addresses
+    // that are always valid (gemm_index.h), and values are masked instead.
+    const DecodeBShape bs{KC, NS, a.n_slabs, kGated ? 1 : 0, a.I, a.L, a.r, a.rp,
+                          a.E_l, a.n_canon, a.lb_shared};
     const uint16_t *lb = a.LB ? a.LB : a.Wp;
     auto load_b = [&](int vc, u32x4 (&b)[NS]) {
         const bool main = vc < nm;  // uniform
-        const int kc = wave + 4 * min(vc, nm - 1);
-        const int g = ((vc - nm) * 4 + wave) * 32 + (lane >> 4) * 8;
-        const int aid = main ? 0 : g / a.rp;
-        const int q0 = main ? 0 : g - aid * a.rp;
-        const int aid_c = max(min(aid, a.L - 1), 0);
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
-            const uint16_t *pm = wbase + ((size_t)kc * NS + n) * 512;
-            const int col = kGated ? (n & 1) * a.I + (slab * 2 + (n >> 1)) * 16 + (lane & 15)
-                                   : (slab * NS + n) * 16 + (lane & 15);
-            const size_t stack = a.lb_shared ? (size_t)aid_c : (size_t)aid_c * a.E_l + le;
-            const uint16_t *pe = lb + (stack * a.n_canon + col) * a.r;
+            const DecodeBLoad d = decode_b_load(bs, wave, lane, vc, nm, le, slab, n);
             if (kRank8) {
-                // past the last adapter (aid >= L) the clamped stack is read; its
+                // past the last adapter (aid >= L) the last stack is read; its
                 // K positions meet zero activations, so it adds nothing
-                b[n] = load16_stream(main ? pm : pe + q0);
+                b[n] = load16_stream((main ? a.Wp : lb) + d.off16);
             } else {  // rank not a multiple of 8: the expand rows need 2-byte loads
-                const u32x4 vm = load16_stream(pm);
+                const u32x4 vm = load16_stream(a.Wp + d.off16);
+                const uint16_t *pe = lb + d.lora_row;
                 uint32_t w[4];
 #pragma unroll
                 for (int i = 0; i < 8; i += 2) {
-                    const uint32_t lo = pe[min(q0 + i, a.r - 1)];
-                    const uint32_t hi = pe[min(q0 + i + 1, a.r - 1)];
-                    w[i >> 1] = (q0 + i < a.r ? lo : 0u) | ((q0 + i + 1 < a.r ? hi : 0u) << 16);
+                    const uint32_t lo = pe[min(d.q0 + i, a.r - 1)];
+                    const uint32_t hi = pe[min(d.q0 + i + 1, a.r - 1)];
+                    w[i >> 1] = (d.q0 + i < a.r ? lo : 0u) | ((d.q0 + i + 1 < a.r ? hi : 0u) << 16);
                 }
-                const u32x4 ve = keep_if(u32x4{w[0], w[1], w[2], w[3]}, aid < a.L);
+                const u32x4 ve = keep_if(u32x4{w[0], w[1], w[2], w[3]}, d.aid < a.L);
                 b[n] = main ? vm : ve;
             }
         }
@@ -160,7 +151,7 @@ __global__ __launch_bounds__(256, MT == 1 ? (kRank8 ? MOE_LORA_DECODE_WAVES : 3)
     const uint16_t *sbase = a.S ? a.S : a.X;
     auto load_a = [&](int vc, u32x4 (&av)[MT], bool (&am)[MT]) {
         const bool main = vc < nm;  // uniform
-        const int kc = wave + 4 * min(vc, nm - 1);
+        const int kc = wave + 4 * (main ? vc : 0);
         const int g = ((vc - nm) * 4 + wave) * 32 + (lane >> 4) * 8;
         const int aid = main ? -1 : g / a.rp;
         const int q0 = main ? 0 : g - aid * a.rp;
@@ -181,29 +172,8 @@ __global__ __launch_bounds__(256, MT == 1 ? (kRank8 ? MOE_LORA_DECODE_WAVES : 3)
     store_partials<MT, NS>(part, acc, n_mt, wave, lane);
     __syncthreads();
 
-    if (kGated && a.phase == 1) {
-        // fp32 pre-activation: 4 groups of 8 per row (gate/up pair jj, half c0)
-        for (int item = tid; item < n_rows * 4; item += 256) {
-            const int row = item >> 2;
-            const int jj = (item >> 1) & 1;
-            const int c0 = (item & 1) * 8;
-            float *hrow = a.H + (size_t)(row0 + row) * 2 * a.I + (slab * 2 + jj) * 16 + c0;
-#pragma unroll
-            for (int i = 0; i < 8; i += 4) {
-                f32x4 g, u;
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    g[h] = sum_partials<MT>(part, row, (2 * jj) * 16 + c0 + i + h);
-                    u[h] = sum_partials<MT>(part, row, (2 * jj + 1) * 16 + c0 + i + h);
-                }
-                *reinterpret_cast<f32x4 *>(hrow + i) = g;
-                *reinterpret_cast<f32x4 *>(hrow + a.I + i) = u;
-            }
-        }
-    } else if (kGated) {
-        // 32 activation columns per row: 4 groups of 8 (gate/up pair jj, half c0);
-        // in phase 2 the pre-activation of phase 1 is added first
-        const bool add_h = a.phase == 2;
+    if (kGated) {
+        // 32 activation columns per row: 4 groups of 8 (gate/up pair jj, half c0)
         for (int item = tid; item < n_rows * 4; item += 256) {
             const int row = item >> 2;
             const int jj = (item >> 1) & 1;
@@ -214,14 +184,8 @@ __global__ __launch_bounds__(256, MT == 1 ? (kRank8 ? MOE_LORA_DECODE_WAVES : 3)
                 float v[2];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    float gate = sum_partials<MT>(part, row, (2 * jj) * 16 + c0 + i + h);
-                    float up = sum_partials<MT>(part, row, (2 * jj + 1) * 16 + c0 + i + h);
-                    if (add_h) {
-                        const float *hrow = a.H + (size_t)(row0 + row) * 2 * a.I +
-                                            (slab * 2 + jj) * 16 + c0 + i + h;
-                        gate += hrow[0];
-                        up += hrow[a.I];
-                    }
+                    const float gate = sum_partials<MT>(part, row, (2 * jj) * 16 + c0 + i + h);
+                    const float up = sum_partials<MT>(part, row, (2 * jj + 1) * 16 + c0 + i + h);
                     v[h] = silu_f32(gate) * up;
                 }
                 packed[i >> 1] = float_to_bf16_bits(v[0]) | (float_to_bf16_bits(v[1]) << 16);
@@ -333,22 +297,11 @@ hipError_t launch_shrink(const ShrinkArgs &a, hipStream_t s)
         return hipSuccess;
     if (shrink_uses_wide(a))
         return launch_shrink_wide(a, (a.n_slots + blocks - 1) / blocks, s);
-    const int mt = shrink_row_tiles(a);
-    if (a.r <= 16) {
-        if (mt == 1)
-            hipLaunchKernelGGL((lora_shrink_kernel<1, 8, 1>), dim3(blocks), dim3(256), 0, s, a);
-        else if (mt == 2)
-            hipLaunchKernelGGL((lora_shrink_kernel<1, 4, 2>), dim3(blocks), dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((lora_shrink_kernel<1, 4, 3>), dim3(blocks), dim3(256), 0, s, a);
-    } else {
-        if (mt == 1)
-            hipLaunchKernelGGL((lora_shrink_kernel<4, 2, 1>), dim3(blocks), dim3(256), 0, s, a);
-        else if (mt == 2)
-            hipLaunchKernelGGL((lora_shrink_kernel<4, 2, 2>), dim3(blocks), dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((lora_shrink_kernel<4, 2, 3>), dim3(blocks), dim3(256), 0, s, a);
-    }
+    with_shrink_shape(a.r, shrink_row_tiles(a), [&](auto ns, auto ch, auto mt) {
+        hipLaunchKernelGGL((lora_shrink_kernel<decltype(ns)::value, decltype(ch)::value,
+                                               decltype(mt)::value>),
+                           dim3(blocks), dim3(256), 0, s, a);
+    });
     return hipGetLastError();
 }
 

@@ -103,17 +103,13 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
     const int KC = a.K >> 5;
     const bool lora = a.S != nullptr && a.L > 0 && a.r > 0;
     const int n_ext = lora ? (a.L * a.rp + 31) >> 5 : 0;
-    const int nv = KC + n_ext;
-    // chunks of this launch: main K only (phase 1), expand only (phase 2), or all
-    const int vbeg = a.phase == 2 ? KC : 0;
-    const int vend = a.phase == 1 ? KC : nv;
+    const int nv = KC + n_ext;  // main K chunks, then the LoRA expand chunks
     // The block's chunk sequence q = 0 .. nq - 1 runs the slabs in turn:
-    // slab slab0 + q / nvs, chunk vbeg + q % nvs.  Every chunk carries the same
-    // loads (the rows are the same for all slabs), so the producers' wait
-    // counts do not change across slabs, and they run on into the next slab
-    // while the consumers finish the previous one.
-    const int nvs = vend - vbeg;
-    const int nq = n_sl * nvs;
+    // slab slab0 + q / nv, chunk q % nv.  Every chunk carries the same loads
+    // (the rows are the same for all slabs), so the producers' wait counts
+    // do not change across slabs, and they run on into the next slab while
+    // the consumers finish the previous one.
+    const int nq = n_sl * nv;
 
     // rows of this tile: slot, source row, adapter (rows past the tile
     // repeat the last row and carry no adapter)
@@ -220,18 +216,18 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
         // outstanding.  (si, vc): the next chunk to issue.
         auto run = [&](auto na) __attribute__((always_inline)) {
             constexpr int kLoads = decltype(na)::value + kNTW;
-            int si = 0, vc = vbeg, st = 0;
+            int si = 0, vc = 0, st = 0;
             auto issue_next = [&]() __attribute__((always_inline)) {
                 const bool past = si >= n_sl;
                 const int s_i = past ? n_sl - 1 : si;
-                const int v_i = past ? vend - 1 : vc;
+                const int v_i = past ? nv - 1 : vc;
                 if (v_i < KC)
                     issue(na, std::true_type{}, s_i, v_i, st);
                 else
                     issue(na, std::false_type{}, s_i, v_i, st);
                 st = st == kStages - 1 ? 0 : st + 1;
-                if (!past && ++vc == vend) {
-                    vc = vbeg;
+                if (!past && ++vc == nv) {
+                    vc = 0;
                     ++si;
                 }
             };
@@ -311,7 +307,7 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
             }
         };
 
-        for (int vc = vbeg; vc < vend; ++vc) {
+        for (int vc = 0; vc < nv; ++vc) {
             dma_wait_barrier<63>();  // the chunk has landed; this wave's reads of the previous one are done
             compute(st, vc < KC ? main_tiles : ext_tiles(vc, main_tiles));
             st = st == kStages - 1 ? 0 : st + 1;
@@ -319,33 +315,12 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
 
         // Epilogue of this slab (the producers meanwhile fill the stages with
         // the next slab's first chunks).  Lane holds rows 4 (lane / 16) + i of
-        // each M tile, column lane % 16 of its four tiles.  Phase 1 writes the
-        // fp32 pre-activation element by element; otherwise each M tile's
-        // bf16 outputs (SwiGLU'd for gate_up) go through this consumer's
-        // private LDS tile, 16 rows x kOut columns, and leave as 16-byte row
-        // segments.
+        // each M tile, column lane % 16 of its four tiles.  Each M tile's bf16
+        // outputs (SwiGLU'd for gate_up) go through this consumer's private
+        // LDS tile, 16 rows x kOut columns, and leave as 16-byte row segments.
         if (!has_cols)
             continue;
         const int c = ln & 15;
-        if (kGated && a.phase == 1) {
-#pragma unroll
-            for (int m = 0; m < kWMT; ++m) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = m * 16 + 4 * (ln >> 4) + i;
-                    if (m < n_mt && r < n_rows) {
-                        const size_t p = (size_t)(row0 + r);
-#pragma unroll
-                        for (int q = 0; q < kNTW / 2; ++q) {
-                            const size_t h_at = p * 2 * a.I + (2 * s64 + q) * 16 + c;
-                            a.H[h_at] = acc[m][2 * q][i];
-                            a.H[h_at + a.I] = acc[m][2 * q + 1][i];
-                        }
-                    }
-                }
-            }
-            continue;
-        }
         constexpr int kOut = kGated ? kNTW / 2 * 16 : kNTW * 16;  // output columns: 32 or 64
         constexpr int kSeg = kOut / 8;                            // 16-byte segments per row
         uint16_t *ot = otile[g];
@@ -361,13 +336,7 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
                     if (kGated) {
 #pragma unroll
                         for (int q = 0; q < kNTW / 2; ++q) {
-                            float gate = acc[m][2 * q][i], up = acc[m][2 * q + 1][i];
-                            if (a.phase == 2 && m * 16 + rr < n_rows) {
-                                const size_t h_at =
-                                    (size_t)(row0 + m * 16 + rr) * 2 * a.I + (2 * s64 + q) * 16 + c;
-                                gate += a.H[h_at];
-                                up += a.H[h_at + a.I];
-                            }
+                            const float gate = acc[m][2 * q][i], up = acc[m][2 * q + 1][i];
                             ot[rr * kOut + q * 16 + c] =
                                 (uint16_t)float_to_bf16_bits(silu_f32(gate) * up);
                         }

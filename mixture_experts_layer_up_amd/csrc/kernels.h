@@ -117,12 +117,6 @@ struct GemmArgs {
     int slabs_per_block;      // wide kernel: adjacent slabs one block runs in turn (set by its launcher)
     const uint16_t *zeros;    // kZeroBytes of zeros
     int lb_shared;            // LB holds one stack per adapter ([L, 1, n_canon, r])
-    // Split gate_up (the two-stream schedule): phase 1 runs the main K only
-    // and writes the fp32 pre-activation h [n, 2I] (gate columns, then up) to
-    // H; phase 2 runs the LoRA expand chunks only, adds H and applies
-    // SwiGLU.  Phase 0 does both in one pass.
-    int phase;
-    float *H;
 };
 
 // Rows per GEMM work-list tile: 16 for the decode-shaped kernel (few rows
@@ -159,6 +153,17 @@ int shrink_row_tiles(const ShrinkArgs &a);
 // launch; permute_shrink_fusable says whether the shapes allow it.
 bool permute_shrink_fusable(const PermuteArgs &pa, const ShrinkArgs &sa);
 hipError_t launch_permute_shrink(const PermuteArgs &pa, const ShrinkArgs &sa, hipStream_t s);
+// The same few-row gate_up shrink from the routing alone (ids, mapping), on
+// a launch of its own: the side stream of the two-stream schedule.  Every
+// row is computed as by the permute's fused launch and by launch_shrink's
+// few-row kernel, bit for bit.  Up to kShrinkByIdsMaxSlots slots.
+constexpr int kShrinkByIdsMaxSlots = 2048;
+// The two-stream schedule is for decode-shaped batches: at most this many
+// tokens (the pages' decode gate), and the slot and segment sizes the
+// side-stream shrink takes (shrink_by_ids_supported).
+constexpr int kTwoStreamMaxTokens = 256;
+bool shrink_by_ids_supported(const PermuteArgs &pa, const ShrinkArgs &sa);
+hipError_t launch_shrink_by_ids(const PermuteArgs &pa, const ShrinkArgs &sa, hipStream_t s);
 // the shrink for segments of many rows: rank r <= 64, mean_rows per segment
 bool shrink_wide_supported(int r);
 hipError_t launch_shrink_wide(const ShrinkArgs &a, int mean_rows, hipStream_t s);

@@ -12,6 +12,8 @@
 // shrink intermediate has one rank-r row per (token, top-k choice)).
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "mfma_pipeline.h"
@@ -111,6 +113,32 @@ __device__ __forceinline__ void shrink_rows(const ShrinkArgs &a, int stack, int 
                         u32x4{packed[0], packed[1], packed[2], packed[3]});
             }
         }
+    }
+}
+
+// The few-row shrink's tile shape for rank r with mt M tiles per pass (NS
+// rank tiles of 16 per pass over N, CH K chunks per pipeline stage): every
+// launch of shrink_rows takes it from here, so that they all compute each
+// row alike, bit for bit.  f(NS, CH, MT) receives std::integral_constant
+// values.
+template <typename F>
+__host__ __forceinline__ void with_shrink_shape(int r, int mt, F f)
+{
+    using std::integral_constant;
+    if (r <= 16) {
+        if (mt == 1)
+            f(integral_constant<int, 1>{}, integral_constant<int, 8>{}, integral_constant<int, 1>{});
+        else if (mt == 2)
+            f(integral_constant<int, 1>{}, integral_constant<int, 4>{}, integral_constant<int, 2>{});
+        else
+            f(integral_constant<int, 1>{}, integral_constant<int, 4>{}, integral_constant<int, 3>{});
+    } else {
+        if (mt == 1)
+            f(integral_constant<int, 4>{}, integral_constant<int, 2>{}, integral_constant<int, 1>{});
+        else if (mt == 2)
+            f(integral_constant<int, 4>{}, integral_constant<int, 2>{}, integral_constant<int, 2>{});
+        else
+            f(integral_constant<int, 4>{}, integral_constant<int, 2>{}, integral_constant<int, 3>{});
     }
 }
 

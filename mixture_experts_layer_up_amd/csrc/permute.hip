@@ -24,7 +24,7 @@
 // lanes of the group with the same key.  With G == 1 the rank kernel's own
 // histogram is the whole one and the count kernel is skipped, and in the
 // forward pass the rank pass shares its launch with the gate_up LoRA shrink
-// (permute_shrink_kernel, below).
+// (permute_shrink_kernel, below), which needs only the routing.
 #include "device_common.h"
 #include "kernels.h"
 #include "lora_shrink_rows.h"
@@ -359,13 +359,57 @@ __global__ __launch_bounds__(kThreads) void permute_rank_kernel(PermuteArgs a)
     permute_rank_body<kMaxKeys, kMaxExperts>(a, blockIdx.y == 1, blockIdx.x);
 }
 
-// The permute and the gate_up LoRA shrink in one launch, for batches of one
-// slot block.  The shrink reads only the routing (ids, adapter mapping), not
-// the permute's output: each of its blocks owns one virtual expert (adapter
-// l, local expert e), finds its slots by scanning the ids itself and writes
-// S by slot.  So the shrink runs beside the permute instead of after it, and
-// one launch boundary goes.  Blocks 0 and 1 are the permute's two key types;
-// block 2 + l * E_l + e is virtual expert (l, e).  Requires T * k <=
+// The gate_up LoRA shrink straight from the routing: it reads the expert ids
+// and the adapter mapping, not the permute's output.  Block s owns virtual
+// expert s = l * E_l + e (adapter l, local expert e); it finds its slots by
+// scanning the ids itself (kSPT slots per thread, all loads issued before
+// any is used), compacts them in ascending slot order in LDS, and runs the
+// shrink body, which writes S by slot.  A slot belongs to the block when its
+// id is expert e and its token's adapter is l, so out-of-range ids and
+// adapters never match, as in the permute's keys.  Needs T * k <= 256 kSPT.
+template <int NS, int CH, int MT, int kSPT>
+__device__ __forceinline__ void shrink_by_ids_body(const PermuteArgs &pa, const ShrinkArgs &sa,
+                                                   int seg)
+{
+    __shared__ float part[Part<MT>::kFloats];
+    __shared__ int row_slot[16 * MT];
+    __shared__ int list[kSPT * kThreads];
+    __shared__ int wave_tot[kWaves];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid >> 6;
+    const int l = seg / pa.E_l;
+    const int want = pa.off + (seg - l * pa.E_l);  // global id of expert e
+    const int n = pa.T * pa.k;
+    int id[kSPT], ad[kSPT];
+#pragma unroll
+    for (int i = 0; i < kSPT; ++i) {
+        const int x = kSPT * tid + i;
+        id[i] = x < n ? pa.topk_ids[x] : -1;
+        ad[i] = (x < n && pa.mapping) ? pa.mapping[x / pa.k] : -1;
+    }
+    int hit = 0;
+#pragma unroll
+    for (int i = 0; i < kSPT; ++i)
+        hit |= (kSPT * tid + i < n && id[i] == want && ad[i] == l) ? 1 << i : 0;
+    const int c = __popc(hit);
+    int total;
+    int pos = block_scan(c, lane, wave, wave_tot, total) - c;
+#pragma unroll
+    for (int i = 0; i < kSPT; ++i)
+        if ((hit >> i) & 1)
+            list[pos++] = kSPT * tid + i;  // ascending slot order
+    if (total == 0)
+        return;
+    __syncthreads();  // list
+    const int stack = sa.a_shared ? l : seg;
+    shrink_rows<NS, CH, MT>(sa, stack, total, [&](int i) { return list[i]; }, part, row_slot);
+}
+
+// The permute and the gate_up shrink in one launch, for batches of one slot
+// block: blocks 0 and 1 are the permute's two key types, block 2 + s runs
+// the shrink of virtual expert s.  The shrink then runs beside the permute
+// instead of after it, and one launch boundary goes.  Requires T * k <=
 // kPermuteSlotsPerBlock and E_l, L * E_l <= kFusedKeys.
 template <int NS, int CH, int MT>
 __global__ __launch_bounds__(kThreads, 2) void permute_shrink_kernel(PermuteArgs pa, ShrinkArgs sa)
@@ -374,43 +418,15 @@ __global__ __launch_bounds__(kThreads, 2) void permute_shrink_kernel(PermuteArgs
         permute_rank_body<kFusedKeys, kFusedKeys>(pa, blockIdx.x == 1, 0);
         return;
     }
-    __shared__ float part[Part<MT>::kFloats];
-    __shared__ int row_slot[16 * MT];
-    __shared__ int list[kPermuteSlotsPerBlock];
-    __shared__ int wave_tot[kWaves];
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid >> 6;
-    const int seg = blockIdx.x - 2;
-    const int l = seg / pa.E_l;
-    const int want = pa.off + (seg - l * pa.E_l);  // global id of expert e
-    const int n = pa.T * pa.k;
-    // slots 4 tid .. 4 tid + 3; all loads issued before any is used.  A slot
-    // belongs here when its id is expert e and its token's adapter is l (so
-    // out-of-range ids and adapters never match, as in the permute's keys).
-    int id[4], ad[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int x = 4 * tid + i;
-        id[i] = x < n ? pa.topk_ids[x] : -1;
-        ad[i] = (x < n && pa.mapping) ? pa.mapping[x / pa.k] : -1;
-    }
-    int hit = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        hit |= (4 * tid + i < n && id[i] == want && ad[i] == l) ? 1 << i : 0;
-    const int c = __popc(hit);
-    int total;
-    int pos = block_scan(c, lane, wave, wave_tot, total) - c;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        if ((hit >> i) & 1)
-            list[pos++] = 4 * tid + i;  // ascending slot order
-    if (total == 0)
-        return;
-    __syncthreads();  // list
-    const int stack = sa.a_shared ? l : seg;
-    shrink_rows<NS, CH, MT>(sa, stack, total, [&](int i) { return list[i]; }, part, row_slot);
+    shrink_by_ids_body<NS, CH, MT, kPermuteSlotsPerBlock / kThreads>(pa, sa, blockIdx.x - 2);
+}
+
+// The same shrink on its own launch (the side stream of the two-stream
+// schedule), one block per virtual expert.
+template <int NS, int CH, int MT, int kSPT>
+__global__ __launch_bounds__(kThreads, 2) void shrink_by_ids_kernel(PermuteArgs pa, ShrinkArgs sa)
+{
+    shrink_by_ids_body<NS, CH, MT, kSPT>(pa, sa, blockIdx.x);
 }
 
 } // namespace
@@ -425,22 +441,35 @@ bool permute_shrink_fusable(const PermuteArgs &pa, const ShrinkArgs &sa)
 hipError_t launch_permute_shrink(const PermuteArgs &pa, const ShrinkArgs &sa, hipStream_t s)
 {
     const dim3 grid(2 + pa.L * pa.E_l);
-    const int mt = shrink_row_tiles(sa);
-    if (sa.r <= 16) {
-        if (mt == 1)
-            hipLaunchKernelGGL((permute_shrink_kernel<1, 8, 1>), grid, dim3(kThreads), 0, s, pa, sa);
-        else if (mt == 2)
-            hipLaunchKernelGGL((permute_shrink_kernel<1, 4, 2>), grid, dim3(kThreads), 0, s, pa, sa);
+    with_shrink_shape(sa.r, shrink_row_tiles(sa), [&](auto ns, auto ch, auto mt) {
+        hipLaunchKernelGGL((permute_shrink_kernel<decltype(ns)::value, decltype(ch)::value,
+                                                  decltype(mt)::value>),
+                           grid, dim3(kThreads), 0, s, pa, sa);
+    });
+    return hipGetLastError();
+}
+
+bool shrink_by_ids_supported(const PermuteArgs &pa, const ShrinkArgs &sa)
+{
+    return pa.T * pa.k <= kShrinkByIdsMaxSlots && sa.r > 0 && sa.L == pa.L &&
+           sa.E_l == pa.E_l && !shrink_uses_wide(sa);
+}
+
+hipError_t launch_shrink_by_ids(const PermuteArgs &pa, const ShrinkArgs &sa, hipStream_t s)
+{
+    const int blocks = pa.L * pa.E_l;
+    if (blocks <= 0)
+        return hipSuccess;
+    const bool small = pa.T * pa.k <= kPermuteSlotsPerBlock;
+    with_shrink_shape(sa.r, shrink_row_tiles(sa), [&](auto ns, auto ch, auto mt) {
+        constexpr int NS = decltype(ns)::value, CH = decltype(ch)::value, MT = decltype(mt)::value;
+        if (small)
+            hipLaunchKernelGGL((shrink_by_ids_kernel<NS, CH, MT, 4>), dim3(blocks),
+                               dim3(kThreads), 0, s, pa, sa);
         else
-            hipLaunchKernelGGL((permute_shrink_kernel<1, 4, 3>), grid, dim3(kThreads), 0, s, pa, sa);
-    } else {
-        if (mt == 1)
-            hipLaunchKernelGGL((permute_shrink_kernel<4, 2, 1>), grid, dim3(kThreads), 0, s, pa, sa);
-        else if (mt == 2)
-            hipLaunchKernelGGL((permute_shrink_kernel<4, 2, 2>), grid, dim3(kThreads), 0, s, pa, sa);
-        else
-            hipLaunchKernelGGL((permute_shrink_kernel<4, 2, 3>), grid, dim3(kThreads), 0, s, pa, sa);
-    }
+            hipLaunchKernelGGL((shrink_by_ids_kernel<NS, CH, MT, kShrinkByIdsMaxSlots / kThreads>),
+                               dim3(blocks), dim3(kThreads), 0, s, pa, sa);
+    });
     return hipGetLastError();
 }
 

@@ -18,6 +18,14 @@ def cached_inputs(name: str):
     return make_inputs(CONFIGS[name])
 
 
+@functools.lru_cache(maxsize=None)
+def cached_oracle(name: str):
+    """The CPU oracle's output for a named layer config (all rows), computed
+    once per test session."""
+    from oracle import oracle
+    return oracle.forward(CONFIGS[name], cached_inputs(name))
+
+
 def announce(msg: str):
     """Name the case on stdout before its GPU work starts (flushed)."""
     sys.stdout.write(f"\n[gpu case] {msg}\n")

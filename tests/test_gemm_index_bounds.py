@@ -1,0 +1,135 @@
+"""Every address the decode-shaped GEMM loads lies inside its buffer.
+
+The decode GEMM issues all of its B-operand loads whatever the chunk kind (a
+main K chunk of the packed weights, or a LoRA expand chunk), so that every
+path keeps the same loads in flight; the address of a load whose value is
+discarded must still be valid.  The addresses come from one definition,
+``csrc/gemm_index.h`` (plain integer arithmetic), which the kernel calls.
+This test compiles that header into a host program, walks every (work item,
+wave, lane, virtual chunk, B tile) of a set of shapes, and checks each load
+against the extent of the buffer it reads: the packed weights
+[E_l, K, N] and the LoRA B stack [L, E_l or 1, N, r].
+
+The shapes include the ones where a wave has no main chunk at all (K < 128:
+K / 32 chunks for 4 waves), ranks that are not multiples of 8 (2-byte
+expand loads beside a 16-byte load of a weight fragment), expand chunks that
+span two adapters or run past the last one, and the shared-outer B stack.
+No GPU is needed.
+"""
+import os
+import subprocess
+
+import pytest
+
+from mixture_experts_layer_up_amd import build
+
+HARNESS = r"""
+#include <cstdio>
+#include <cstdlib>
+#include "gemm_index.h"
+using namespace moe_lora;
+
+// args: K N gated I L r E_l lb_shared
+int main(int argc, char **argv)
+{
+    if (argc != 9) return 2;
+    const int K = atoi(argv[1]), N = atoi(argv[2]), gated = atoi(argv[3]), I = atoi(argv[4]);
+    const int L = atoi(argv[5]), r = atoi(argv[6]), E_l = atoi(argv[7]), shared = atoi(argv[8]);
+    const int NS = 4, KC = K / 32, n_slabs = N / 64;
+    const bool lora = L > 0 && r > 0;
+    const int rp = lora ? (r + 7) / 8 * 8 : 8;
+    const DecodeBShape s{KC, NS, n_slabs, gated, I, lora ? L : 0, lora ? r : 0, rp, E_l, N, shared};
+    const size_t w_elems = (size_t)E_l * K * N;
+    const size_t lb_elems = lora ? (size_t)L * (shared ? 1 : E_l) * N * r : 0;
+    // the launcher's choice: 16-byte expand loads when r % 8 == 0 (and for r = 0)
+    const bool rank8 = (s.r & 7) == 0;
+    const int n_ext = lora ? (L * rp + 31) / 32 : 0;
+    long long loads = 0, main_loads = 0, ext_loads = 0;
+    const int experts[2] = {0, E_l - 1};
+    for (int ei = 0; ei < 2; ++ei) {
+        const int le = experts[ei];
+        for (int slab = 0; slab < n_slabs; ++slab)
+            for (int wave = 0; wave < 4; ++wave) {
+                const int nm = decode_main_chunks(KC, wave);
+                const int ne = wave < n_ext ? (n_ext - wave + 3) / 4 : 0;
+                for (int vc = 0; vc < nm + ne; ++vc)
+                    for (int lane = 0; lane < 64; ++lane)
+                        for (int n = 0; n < NS; ++n) {
+                            const DecodeBLoad d = decode_b_load(s, wave, lane, vc, nm, le, slab, n);
+                            const size_t lim = d.from_lora ? lb_elems : w_elems;
+                            ++loads;
+                            (vc < nm ? main_loads : ext_loads)++;
+                            if (d.off16 + 8 > lim) {
+                                printf("OOB 16-byte load: le=%d slab=%d wave=%d vc=%d nm=%d lane=%d n=%d "
+                                       "from_lora=%d off=%zu size=%zu\n", le, slab, wave, vc, nm, lane,
+                                       n, d.from_lora, d.off16, lim);
+                                return 1;
+                            }
+                            if (!rank8) {  // 2-byte loads of the expand row, on every chunk
+                                for (int i = 0; i < 8; ++i) {
+                                    const int q = d.q0 + i < r - 1 ? d.q0 + i : r - 1;
+                                    if (q < 0 || d.lora_row + q >= lb_elems) {
+                                        printf("OOB 2-byte load: le=%d slab=%d wave=%d vc=%d lane=%d "
+                                               "n=%d q=%d row=%zu size=%zu\n", le, slab, wave, vc,
+                                               lane, n, q, d.lora_row, lb_elems);
+                                        return 1;
+                                    }
+                                }
+                            }
+                            // a main chunk reads its own fragment of this item's slab
+                            if (vc < nm) {
+                                const size_t slab_lo = ((size_t)le * n_slabs + slab) * KC * NS * 512;
+                                if (d.from_lora || d.off16 < slab_lo ||
+                                    d.off16 + 8 > slab_lo + (size_t)KC * NS * 512) {
+                                    printf("main chunk outside its slab: le=%d slab=%d vc=%d\n",
+                                           le, slab, vc);
+                                    return 1;
+                                }
+                            }
+                        }
+            }
+    }
+    printf("ok %lld loads (%lld main, %lld expand)\n", loads, main_loads, ext_loads);
+    return 0;
+}
+"""
+
+# (name, K, N, gated, I, L, r, E_l, shared)
+SHAPES = [
+    # the tiny layer (H 128, I 64, rank 4: the 2-byte expand loads); its down
+    # GEMM has K = 64, so waves 2 and 3 have no chunk at all
+    ("tiny_gate_up", 128, 128, 1, 64, 2, 4, 8, 0),
+    ("tiny_down", 64, 128, 0, 64, 2, 4, 8, 0),
+    # waves with expand chunks but no main chunk, with the 2-byte expand
+    # loads: the 16-byte load must not read before the slab
+    ("inter32_down_r12", 32, 320, 0, 32, 3, 12, 16, 0),
+    ("k64_down_r20_four_adapters", 64, 128, 0, 64, 4, 20, 8, 0),
+    ("inter96_down_r8", 96, 320, 0, 96, 3, 8, 16, 0),
+    ("mid_gate_up_r12", 320, 192, 1, 96, 3, 12, 16, 0),
+    ("r24_three_adapters", 256, 384, 1, 192, 3, 24, 4, 0),
+    ("r20_shared_outer_down", 96, 256, 0, 96, 2, 20, 8, 1),
+    ("r4_shared_outer_down", 64, 128, 0, 64, 2, 4, 8, 1),
+    ("no_lora", 64, 128, 0, 64, 0, 0, 8, 0),
+    ("decode64_gate_up", 2048, 1536, 1, 768, 4, 16, 128, 0),
+    ("decode64_down", 768, 2048, 0, 768, 4, 16, 128, 0),
+    ("rank_256_one_adapter", 128, 128, 1, 64, 1, 256, 2, 0),
+]
+
+
+@pytest.fixture(scope="module")
+def harness(tmp_path_factory):
+    d = tmp_path_factory.mktemp("gemm_index")
+    src = d / "bounds.cpp"
+    src.write_text(HARNESS)
+    exe = d / "bounds"
+    subprocess.run(["g++", "-O1", "-std=c++17", f"-I{build.CSRC}", str(src), "-o", str(exe)],
+                   check=True, capture_output=True)
+    return str(exe)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: s[0])
+def test_decode_gemm_b_loads_in_bounds(harness, shape):
+    name, *args = shape
+    res = subprocess.run([harness, *map(str, args)], capture_output=True, text=True)
+    assert res.returncode == 0, f"{name}: {res.stdout.strip()}"
+    assert res.stdout.startswith("ok"), res.stdout

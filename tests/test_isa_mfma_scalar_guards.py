@@ -1,10 +1,18 @@
-"""MFMA instructions ignore the EXEC mask, so no MFMA may sit in a region of
-the gfx950 code where EXEC has been narrowed for a branch.  A guard that the
-compiler lowers to EXEC masking (because it cannot see that the condition is
-wave-uniform) would let the MFMA run for the whole wave anyway.
+"""Properties of the gfx950 assembly that the kernels rely on (no GPU needed).
 
-This compiles the kernels to gfx950 assembly (no GPU needed) and checks every
-MFMA.
+1. MFMA instructions ignore the EXEC mask, so no MFMA may sit in a region of
+   the code where EXEC has been narrowed for a branch.  A guard that the
+   compiler lowers to EXEC masking (because it cannot see that the condition
+   is wave-uniform) would let the MFMA run for the whole wave anyway.  Every
+   MFMA is checked.
+2. The direct global->LDS loads are inline assembly that set M0 (the LDS
+   address) and issue the load in one statement.  M0 is a register the
+   compiler reserves: it is not told that the statement overwrites it, so any
+   instruction of its own that reads or writes M0 could see a clobbered
+   value.  In the kernels that use those loads, M0 may appear only in the
+   statement's own `s_mov_b32 m0` directly followed by its
+   `global_load_lds_dwordx4`, and no instruction that reads M0 implicitly
+   (relative moves, messages, GWS, LDS parameter loads) may appear at all.
 """
 import os
 import re
@@ -17,6 +25,8 @@ from mixture_experts_layer_up_amd import build
 # every source with MFMA code (the permute launch also runs the gate_up shrink)
 SOURCES = [f for f in build.sources()
            if "expert_gemm" in f or "lora_shrink" in f or "permute" in f]
+# every source that includes the direct-load header
+DMA_SOURCES = [f for f in build.sources() if '#include "lds_dma.h"' in open(f).read()]
 
 
 def _device_asm(src, tmp_path):
@@ -129,3 +139,45 @@ def test_no_mfma_under_exec_mask(src, tmp_path):
     bad, total = _mfma_under_exec_mask(_device_asm(src, tmp_path))
     assert total > 0
     assert not bad, f"{len(bad)} of {total} MFMAs sit under an EXEC mask: {bad[:3]}"
+
+
+# instructions that read M0 without naming it
+_IMPLICIT_M0 = re.compile(r"^(s_movrel|v_movrel|s_sendmsg|ds_gws|ds_ordered|s_ttracedata|"
+                          r"ds_param|v_interp|s_cbranch_g_fork)")
+
+
+def _m0_violations(asm):
+    lines = [ln.split(";")[0].strip() for ln in asm.splitlines()]
+    lines = [t for t in lines if t and not t.startswith(".")]
+    bad, pairs = [], 0
+    i = 0
+    while i < len(lines):
+        t = lines[i]
+        if re.match(r"^s_mov_b32\s+m0,", t):
+            nxt = lines[i + 1] if i + 1 < len(lines) else ""
+            if nxt.startswith("global_load_lds_dwordx4"):
+                pairs += 1
+                i += 2
+                continue
+            bad.append(t)
+        elif re.search(r"\bm0\b", t) or _IMPLICIT_M0.match(t):
+            bad.append(t)
+        i += 1
+    return bad, pairs
+
+
+@pytest.mark.parametrize("src", DMA_SOURCES, ids=os.path.basename)
+def test_m0_only_in_direct_load_statements(src, tmp_path):
+    bad, pairs = _m0_violations(_device_asm(src, tmp_path))
+    assert pairs > 0
+    assert not bad, f"M0 used outside the direct-load statements: {bad[:5]}"
+
+
+def test_m0_checker_flags_other_uses():
+    """The checker itself: a compiler-style M0 write, an implicit reader, and
+    an M0 write not followed by the direct load are all flagged."""
+    ok = "s_mov_b32 m0, s4\nglobal_load_lds_dwordx4 v[2:3], off\n"
+    assert _m0_violations(ok) == ([], 1)
+    assert _m0_violations(ok + "s_mov_b32 m0, -1\nds_read_b32 v1, v2\n")[0]
+    assert _m0_violations(ok + "v_movrels_b32 v0, v1\n")[0]
+    assert _m0_violations(ok + "v_readlane_b32 s0, v1, m0\n")[0]

@@ -52,6 +52,8 @@ extern "C" {
 #define MOE_LORA_ERR_WORKSPACE_TOO_SMALL -3
 #define MOE_LORA_ERR_MISALIGNED          -4 /* pointer not aligned as required */
 #define MOE_LORA_ERR_HIP                 -5 /* a HIP launch or event call failed */
+#define MOE_LORA_ERR_SCRATCH_LIMIT       -6 /* moe_lora_forward_no_alloc: the shape needs more
+                                               than MOE_LORA_STATIC_SCRATCH_BYTES of workspace */
 
 /* Number of events moe_lora_forward records when moe_lora_inputs.stage_events
  * is set: before routing, then after each of routing+permute, gate_up LoRA
@@ -300,6 +302,32 @@ int moe_lora_route(const moe_lora_shape *shape, const float *router_logits,
 int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *inputs,
                      const moe_lora_routing *routing, void *out, void *workspace,
                      size_t workspace_bytes, void *stream);
+
+/*
+ * The layer forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): moe_lora_forward with the workspace taken from a static
+ * array inside the library instead of from the caller.  Arguments, outputs
+ * and results are those of moe_lora_forward (same kernels, bitwise the same
+ * output); the caller still passes every input and output.
+ *   - The array holds MOE_LORA_STATIC_SCRATCH_BYTES bytes per GPU; a shape
+ *     whose moe_lora_workspace_size exceeds that returns
+ *     MOE_LORA_ERR_SCRATCH_LIMIT before any HIP call (at hidden 2048,
+ *     inter 768 and rank 16 that is about 2900 slots, T * top_k).
+ *   - It uses the array of the current device, which must be the device of
+ *     `stream`.  The first call on a device looks up that device's copy
+ *     (hipGetSymbolAddress; the library then holds it until the process
+ *     ends); no call allocates or frees memory.
+ *   - Every call on one GPU shares that GPU's array, whose contents the next
+ *     call overwrites: calls that may overlap on one GPU (on different
+ *     streams, or from several threads without ordering) race, so a caller
+ *     orders them (one stream, or events).  The forward needs nothing in the
+ *     array to start at zero.
+ */
+#define MOE_LORA_STATIC_SCRATCH_BYTES (16u << 20)
+
+int moe_lora_forward_no_alloc(const moe_lora_shape *shape, const moe_lora_inputs *inputs,
+                              const moe_lora_routing *routing, void *out, void *stream);
 
 /*
  * The finalize on its own ("BF16 support for the experimental_sgl_trtllm

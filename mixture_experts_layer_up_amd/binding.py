@@ -57,6 +57,7 @@ class Inputs(ctypes.Structure):
 
 
 NUM_STAGE_EVENTS = 7
+STATIC_SCRATCH_BYTES = 16 << 20  # MOE_LORA_STATIC_SCRATCH_BYTES
 FLAG_EXPERT_ID = 1   # a given top-k id outside [-1, num_experts)
 FLAG_ADAPTER = 2     # a token_lora_mapping value outside [-1, num_loras)
 STAGE_NAMES = ("route_permute", "lora_shrink_gate_up", "gemm_gate_up_swiglu",
@@ -94,6 +95,8 @@ def load_library(path: str = LIB_PATH):
     lib.moe_lora_route.restype = ctypes.c_int
     lib.moe_lora_forward.argtypes = [P(Shape), P(Inputs), P(Routing), vp, vp, ctypes.c_size_t, vp]
     lib.moe_lora_forward.restype = ctypes.c_int
+    lib.moe_lora_forward_no_alloc.argtypes = [P(Shape), P(Inputs), P(Routing), vp, vp]
+    lib.moe_lora_forward_no_alloc.restype = ctypes.c_int
     lib.moe_lora_finalize.argtypes = [P(Shape), vp, vp, vp, vp, vp]
     lib.moe_lora_finalize.restype = ctypes.c_int
     lib.moe_lora_strerror.argtypes = [ctypes.c_int]
@@ -211,34 +214,14 @@ def route(shape: Shape, router_logits: Optional[torch.Tensor] = None,
     return r
 
 
-def forward(shape: Shape, hidden: torch.Tensor, w13_packed: torch.Tensor,
-            w2_packed: torch.Tensor, lora_a_gate_up=None, lora_b_gate_up=None,
-            lora_a_down=None, lora_b_down=None, token_lora_mapping=None,
-            router_logits=None, topk_ids=None, topk_weights=None, routing_bias=None,
-            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-            routing: Optional[Dict[str, torch.Tensor]] = None,
-            stage_events: Optional[Sequence[int]] = None,
-            expert_out: Optional[torch.Tensor] = None,
-            side_stream: Optional[int] = None, fork_event: Optional[int] = None,
-            join_event: Optional[int] = None,
-            input_flags: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
-    """One layer forward on the current stream; returns ``out`` bf16 [T, H].
-
-    With ``expert_out`` (bf16 [T*k, H]) the per-slot expert outputs are
-    written there at their permuted rows and the finalize is skipped (returns
-    None; needs ``routing``); :func:`finalize` completes it.  ``side_stream``,
-    ``fork_event``, ``join_event`` (raw hipStream_t / hipEvent_t handles)
-    select the two-stream schedule for the gate_up LoRA.  ``input_flags``
-    (int32, one element) receives the MOE_LORA_FLAG_* bits (ORed in).
-    """
+def _inputs(shape: Shape, hidden, w13_packed, w2_packed, lora_a_gate_up, lora_b_gate_up,
+            lora_a_down, lora_b_down, token_lora_mapping, router_logits, topk_ids, topk_weights,
+            routing_bias, stage_events, expert_out, side_stream, fork_event, join_event,
+            input_flags):
+    """The moe_lora_inputs struct of one forward call (keeps its event array alive)."""
     T, H, I, E, k = shape.num_tokens, shape.hidden, shape.inter, shape.num_experts, shape.top_k
     E_l, L, rg, rd = shape.local_num_experts, shape.num_loras, shape.rank_gate_up, shape.rank_down
     outer = 1 if shape.lora_shared_outer else E_l
-    if out is None and expert_out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=hidden.device)
-    ws_bytes = workspace_size(shape)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=hidden.device)
     gu = L > 0 and rg > 0
     dn = L > 0 and rd > 0
     ev = None
@@ -264,8 +247,58 @@ def forward(shape: Shape, hidden: torch.Tensor, w13_packed: torch.Tensor,
         side_stream, fork_event, join_event,
         _ptr(input_flags, torch.int32, (1,), "input_flags"),
     )
+    return inputs, ev
+
+
+def forward(shape: Shape, hidden: torch.Tensor, w13_packed: torch.Tensor,
+            w2_packed: torch.Tensor, lora_a_gate_up=None, lora_b_gate_up=None,
+            lora_a_down=None, lora_b_down=None, token_lora_mapping=None,
+            router_logits=None, topk_ids=None, topk_weights=None, routing_bias=None,
+            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+            routing: Optional[Dict[str, torch.Tensor]] = None,
+            stage_events: Optional[Sequence[int]] = None,
+            expert_out: Optional[torch.Tensor] = None,
+            side_stream: Optional[int] = None, fork_event: Optional[int] = None,
+            join_event: Optional[int] = None,
+            input_flags: Optional[torch.Tensor] = None,
+            no_alloc: bool = False) -> Optional[torch.Tensor]:
+    """One layer forward on the current stream; returns ``out`` bf16 [T, H].
+
+    With ``expert_out`` (bf16 [T*k, H]) the per-slot expert outputs are
+    written there at their permuted rows and the finalize is skipped (returns
+    None; needs ``routing``); :func:`finalize` completes it.  ``side_stream``,
+    ``fork_event``, ``join_event`` (raw hipStream_t / hipEvent_t handles)
+    select the two-stream schedule for the gate_up LoRA.  ``input_flags``
+    (int32, one element) receives the MOE_LORA_FLAG_* bits (ORed in).
+    ``no_alloc``: call moe_lora_forward_no_alloc, whose workspace is the
+    library's static per-device scratch (``workspace`` must then be None);
+    ``out`` (or ``expert_out``) must then be given, since this wrapper would
+    otherwise allocate it.
+    """
+    T, H = shape.num_tokens, shape.hidden
+    if no_alloc:
+        if workspace is not None:
+            raise MoELoRAError("no_alloc takes no workspace")
+        if out is None and expert_out is None:
+            raise MoELoRAError("no_alloc needs a caller-owned out (or expert_out)")
+    elif out is None and expert_out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=hidden.device)
+    inputs, _ev = _inputs(shape, hidden, w13_packed, w2_packed, lora_a_gate_up, lora_b_gate_up,
+                          lora_a_down, lora_b_down, token_lora_mapping, router_logits, topk_ids,
+                          topk_weights, routing_bias, stage_events, expert_out, side_stream,
+                          fork_event, join_event, input_flags)
     rs = _routing_struct(routing) if routing is not None else None
-    _check(load_library().moe_lora_forward(
+    lib = load_library()
+    if no_alloc:
+        _check(lib.moe_lora_forward_no_alloc(
+            ctypes.byref(shape), ctypes.byref(inputs),
+            ctypes.byref(rs) if rs is not None else None,
+            _ptr(out, _BF16, (T, H), "out"), _stream()))
+        return out
+    if workspace is None:
+        workspace = torch.empty(max(workspace_size(shape), 1), dtype=torch.uint8,
+                                device=hidden.device)
+    _check(lib.moe_lora_forward(
         ctypes.byref(shape), ctypes.byref(inputs), ctypes.byref(rs) if rs is not None else None,
         _ptr(out, _BF16, (T, H), "out"), _ptr(workspace, None, None, "workspace"),
         workspace.numel() * workspace.element_size(), _stream()))

@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include "kernels.h"
 #include "moe_lora.h"
@@ -284,26 +285,21 @@ int moe_lora_route(const moe_lora_shape *shape, const float *router_logits,
                            static_cast<hipStream_t>(stream));
 }
 
-int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
-                     const moe_lora_routing *routing, void *out, void *workspace,
-                     size_t workspace_bytes, void *stream)
+} // extern "C"
+
+namespace {
+
+// Every argument check of a forward with tokens, except the workspace's:
+// host code only, before any HIP call.
+int validate_inputs(const moe_lora_shape *shape, const moe_lora_inputs *in,
+                    const moe_lora_routing *routing, const void *out, const void *stream)
 {
-    MOE_TRY(validate_shape(shape));
-    if (!in)
-        return MOE_LORA_ERR_INVALID_ARG;
-    if (shape->num_tokens == 0) {
-        hipStream_t st = static_cast<hipStream_t>(stream);
-        MOE_TRY(enqueue_empty_batch(shape, routing, st));
-        for (int i = 0; i < MOE_LORA_NUM_STAGE_EVENTS; ++i)
-            MOE_TRY(record(in->stage_events, i, st));
-        return MOE_LORA_OK;
-    }
     // expert_out: the per-slot outputs go to the caller and the finalize is
     // skipped; the caller needs the routing export to finalize them
-    void *expert_out = in->expert_out;
+    const void *expert_out = in->expert_out;
     if ((!expert_out && !out) || (expert_out && !routing))
         return MOE_LORA_ERR_INVALID_ARG;
-    if (!workspace || !in->hidden || !in->w13_packed || !in->w2_packed)
+    if (!in->hidden || !in->w13_packed || !in->w2_packed)
         return MOE_LORA_ERR_INVALID_ARG;
     if (in->side_stream && (!in->fork_event || !in->join_event))
         return MOE_LORA_ERR_INVALID_ARG;
@@ -321,7 +317,7 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     if (dn && (!in->lora_a_down || !in->lora_b_down))
         return MOE_LORA_ERR_INVALID_ARG;
     if (!aligned(in->hidden, 16) || !aligned(in->w13_packed, 16) || !aligned(in->w2_packed, 16) ||
-        !aligned(out, 16) || !aligned(expert_out, 16) || !aligned(workspace, kAlign))
+        !aligned(out, 16) || !aligned(expert_out, 16))
         return MOE_LORA_ERR_MISALIGNED;
     if (gu && (!aligned(in->lora_a_gate_up, 16) ||
                !aligned(in->lora_b_gate_up, shape->rank_gate_up % 8 == 0 ? 16 : 2)))
@@ -335,6 +331,33 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
                     !routing->lora_seg_slots ||
                     (from_logits && (!routing->topk_ids || !routing->topk_weights))))
         return MOE_LORA_ERR_INVALID_ARG;
+    return MOE_LORA_OK;
+}
+
+// The layer forward on a workspace the caller or the library provides.
+int forward_impl(const moe_lora_shape *shape, const moe_lora_inputs *in,
+                 const moe_lora_routing *routing, void *out, void *workspace,
+                 size_t workspace_bytes, void *stream)
+{
+    MOE_TRY(validate_shape(shape));
+    if (!in)
+        return MOE_LORA_ERR_INVALID_ARG;
+    if (shape->num_tokens == 0) {
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        MOE_TRY(enqueue_empty_batch(shape, routing, st));
+        for (int i = 0; i < MOE_LORA_NUM_STAGE_EVENTS; ++i)
+            MOE_TRY(record(in->stage_events, i, st));
+        return MOE_LORA_OK;
+    }
+    MOE_TRY(validate_inputs(shape, in, routing, out, stream));
+    if (!workspace)
+        return MOE_LORA_ERR_INVALID_ARG;
+    if (!aligned(workspace, kAlign))
+        return MOE_LORA_ERR_MISALIGNED;
+    void *expert_out = in->expert_out;
+    const bool from_logits = in->router_logits != nullptr;
+    const bool gu = lora_gate_up_active(shape);
+    const bool dn = lora_down_active(shape);
     const Layout lay = make_layout(shape);
     if (workspace_bytes < lay.total)
         return MOE_LORA_ERR_WORKSPACE_TOO_SMALL;
@@ -510,6 +533,60 @@ int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *in,
     return MOE_LORA_OK;
 }
 
+// The allocation-free forward's workspace: one array per device, in the
+// library's code object, MOE_LORA_STATIC_SCRATCH_BYTES long.  Host code never
+// uses the array's name as an address: the device address of each GPU's copy
+// comes from hipGetSymbolAddress, taken once per device (with that device
+// current) and kept here.
+__device__ __align__(256) unsigned char scratch[MOE_LORA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once known
+
+// Device address of the current device's scratch array.
+int current_device_scratch(void **ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return MOE_LORA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return MOE_LORA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return MOE_LORA_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int moe_lora_forward(const moe_lora_shape *shape, const moe_lora_inputs *inputs,
+                     const moe_lora_routing *routing, void *out, void *workspace,
+                     size_t workspace_bytes, void *stream)
+{
+    return forward_impl(shape, inputs, routing, out, workspace, workspace_bytes, stream);
+}
+
+int moe_lora_forward_no_alloc(const moe_lora_shape *shape, const moe_lora_inputs *inputs,
+                              const moe_lora_routing *routing, void *out, void *stream)
+{
+    MOE_TRY(validate_shape(shape));
+    if (!inputs)
+        return MOE_LORA_ERR_INVALID_ARG;
+    if (shape->num_tokens > 0)
+        MOE_TRY(validate_inputs(shape, inputs, routing, out, stream));
+    if (make_layout(shape).total > MOE_LORA_STATIC_SCRATCH_BYTES)
+        return MOE_LORA_ERR_SCRATCH_LIMIT;
+    void *ws = nullptr;
+    MOE_TRY(current_device_scratch(&ws));
+    return forward_impl(shape, inputs, routing, out, ws, MOE_LORA_STATIC_SCRATCH_BYTES, stream);
+}
+
 int moe_lora_finalize(const moe_lora_shape *shape, const void *expert_out,
                       const int32_t *expanded_idx_to_permuted_idx, const float *topk_weights,
                       void *out, void *stream)
@@ -542,6 +619,9 @@ const char *moe_lora_strerror(int status)
         return "pointer not aligned as required";
     case MOE_LORA_ERR_HIP:
         return "HIP launch or event call failed";
+    case MOE_LORA_ERR_SCRATCH_LIMIT:
+        return "shape needs more workspace than the static scratch of moe_lora_forward_no_alloc "
+               "holds (MOE_LORA_STATIC_SCRATCH_BYTES)";
     default:
         return "unknown status";
     }

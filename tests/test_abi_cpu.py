@@ -13,7 +13,7 @@ import pytest
 from mixture_experts_layer_up_amd import binding
 from mixture_experts_layer_up_amd.synth import CONFIGS
 
-ERR_INVALID_ARG, ERR_SHAPE, ERR_WS, ERR_ALIGN = -1, -2, -3, -4
+ERR_INVALID_ARG, ERR_SHAPE, ERR_WS, ERR_ALIGN, ERR_SCRATCH = -1, -2, -3, -4, -6
 
 
 @pytest.fixture(scope="module")
@@ -58,7 +58,7 @@ def test_flag_bits_match_header():
 
 def test_strerror(lib):
     assert lib.moe_lora_strerror(0) == b"ok"
-    for rc in (-1, -2, -3, -4, -5):
+    for rc in (-1, -2, -3, -4, -5, -6):
         assert lib.moe_lora_strerror(rc) not in (b"ok", b"unknown status")
     assert lib.moe_lora_strerror(42) == b"unknown status"
 
@@ -250,3 +250,43 @@ def test_route_workspace_size_and_validation(lib):
                               ctypes.byref(rs), _fake((1 << 20) + 4), need, None) == ERR_ALIGN
     bad = binding.make_shape(cfg.replace(top_k=0))
     assert lib.moe_lora_route_workspace_size(ctypes.byref(bad)) == 0
+
+
+def test_no_alloc_forward_validation(lib):
+    """moe_lora_forward_no_alloc rejects bad arguments, and shapes whose
+    workspace exceeds its static scratch, before any HIP call."""
+    text = open(binding.HEADER_PATH).read()
+    limit = re.search(r"#define MOE_LORA_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert int(limit.group(1)) << int(limit.group(2)) == binding.STATIC_SCRATCH_BYTES
+    assert int(re.search(r"#define MOE_LORA_ERR_SCRATCH_LIMIT\s+(-\d+)", text).group(1)) == ERR_SCRATCH
+    inp = _inputs()
+    prefill = binding.make_shape(CONFIGS["prefill"])
+    assert binding.workspace_size(prefill) > binding.STATIC_SCRATCH_BYTES
+    assert lib.moe_lora_forward_no_alloc(ctypes.byref(prefill), ctypes.byref(inp), None,
+                                         _fake(), None) == ERR_SCRATCH
+    # the largest decode batch that fits, and the first that does not
+    base = CONFIGS["decode64"]
+    fits = [T for T in (64, 256, 360) if
+            binding.workspace_size(binding.make_shape(base.replace(num_tokens=T)))
+            <= binding.STATIC_SCRATCH_BYTES]
+    assert fits == [64, 256, 360]
+    big = binding.make_shape(base.replace(num_tokens=400))
+    assert lib.moe_lora_forward_no_alloc(ctypes.byref(big), ctypes.byref(inp), None, _fake(),
+                                         None) == ERR_SCRATCH
+    shape = binding.make_shape(base)
+    assert lib.moe_lora_forward_no_alloc(ctypes.byref(shape), None, None, _fake(),
+                                         None) == ERR_INVALID_ARG
+    assert lib.moe_lora_forward_no_alloc(None, ctypes.byref(inp), None, _fake(),
+                                         None) == ERR_INVALID_ARG
+    for over, expect in [(dict(hidden=None), ERR_INVALID_ARG),
+                         (dict(hidden=_fake(4096 + 8)), ERR_ALIGN),
+                         (dict(router_logits=None), ERR_INVALID_ARG),
+                         (dict(side_stream=_fake()), ERR_INVALID_ARG)]:
+        bad = _inputs(**over)
+        assert lib.moe_lora_forward_no_alloc(ctypes.byref(shape), ctypes.byref(bad), None,
+                                             _fake(), None) == expect, over
+    assert lib.moe_lora_forward_no_alloc(ctypes.byref(shape), ctypes.byref(inp), None, None,
+                                         None) == ERR_INVALID_ARG     # no out
+    bad_shape = binding.make_shape(base.replace(hidden=96))
+    assert lib.moe_lora_forward_no_alloc(ctypes.byref(bad_shape), ctypes.byref(inp), None,
+                                         _fake(), None) == ERR_SHAPE

@@ -100,15 +100,15 @@ def test_topk_passthrough_with_invalid_ids():
 
 
 
+@pytest.mark.parametrize("T", [77, 40])
 @pytest.mark.parametrize("E,k,method,with_bias", [
     (128, 8, 0, True), (128, 8, 1, False), (128, 8, 1, True), (100, 7, 1, True),
-    (1024, 64, 1, True), (16, 16, 1, False), (33, 3, 0, True)])
-def test_routing_variants(E, k, method, with_bias):
+    (1024, 64, 1, True), (16, 16, 1, False), (33, 3, 0, True), (256, 8, 1, True)])
+def test_routing_variants(E, k, method, with_bias, T):
     """Selection bias (choice only) and softmax over all experts: ids bit-exact,
     weights to 1e-6 (the readings of the pages' undefined routing bias and
-    routing method that the oracle takes)."""
-    announce(f"routing variant E={E} k={k} method={method} bias={with_bias}")
-    T = 77
+    routing method that the oracle takes), at two batch sizes."""
+    announce(f"routing variant T={T} E={E} k={k} method={method} bias={with_bias}")
     cfg = CONFIGS["tiny"].replace(num_tokens=T, num_experts=E, top_k=k, local_num_experts=E,
                                   num_loras=2, routing_method=method)
     rng = np.random.default_rng(E + k + 10 * method)

@@ -146,9 +146,14 @@ def test_external_finalize_small_shapes():
 # kernel before the fork); WIDE (700 tokens) and SLAB_GROUPS (640): above the
 # token gate, so the side stream is not used.
 MID_TOPK = MID.replace(name="mid_topk")
+# a routing bias and the softmax over all experts, with and without the side
+# stream: ids and weights bitwise equal too
+MID_BIAS_M1 = MID.replace(name="mid_bias_m1", routing_method=1, routing_bias_sigma=1.0)
+DECODE64_BIAS = CONFIGS["decode64"].replace(name="decode64_bias", routing_bias_sigma=1.0)
 
 
-@pytest.mark.parametrize("cfg", [MID, SPLIT_FEW, SHARED_MID_EP, MID_TOPK, WIDE, SLAB_GROUPS],
+@pytest.mark.parametrize("cfg", [MID, SPLIT_FEW, SHARED_MID_EP, MID_TOPK, MID_BIAS_M1,
+                                 DECODE64_BIAS, WIDE, SLAB_GROUPS],
                          ids=lambda c: c.name)
 def test_two_stream_bitwise_equals_one_stream(cfg):
     announce(f"forward two-stream {cfg.name}")

@@ -15,16 +15,20 @@
 //    global->LDS loads (global_load_lds_dwordx4), which occupy the issuing
 //    wave for a long time each; on separate waves that time no longer delays
 //    any MFMA.
-//  * K advances in chunks of 32.  kStages chunks are resident in LDS (27 KiB
-//    each: 176 activation rows + the slab's 16 weight fragments); the
-//    producers keep kStages - 1 in flight.  One block barrier per chunk both
-//    publishes a landed chunk (each producer waits for its own loads with an
-//    explicit vmcnt first) and frees the stage the consumers finished.
-//  * Activation rows are stored 64 bytes apart with the four 16-byte K
-//    quarters of a row XOR-swizzled by bits 1..3 of the row, so the 16-row
-//    MFMA fragment reads hit distinct LDS banks; a direct load writes 1 KiB
-//    contiguously, which is bank-conflict free by construction.  Rows of M
-//    tiles past the tile are not loaded at all.
+//  * K advances in chunks of 32.  Two LDS rings: the slab's 16 weight
+//    fragments of a chunk (16 KiB; 5 stages), and the activation rows of a
+//    chunk pair (176 rows x 128 bytes = 22 KiB; 3 stages), so each row
+//    arrives as whole 128-byte lines, 8 rows per direct load: the per-CU
+//    request path, not HBM, bounded the loads of half lines (16 rows x 64
+//    bytes per load).  The producers keep 4 chunks in flight.  One block
+//    barrier per chunk both publishes a landed chunk (each producer waits
+//    for its own loads with an explicit vmcnt first) and frees the stages
+//    the consumers finished.
+//  * The eight 16-byte K pieces of an activation row are XOR-swizzled by
+//    bits 1..3 of the row, so the 16-row MFMA fragment reads hit distinct
+//    LDS banks; a direct load writes 1 KiB contiguously, which is
+//    bank-conflict free by construction.  Rows of M tiles past the tile are
+//    not loaded at all.
 //  * LoRA expand chunks follow the main K chunks.  A row's expand values are
 //    kept only in the K block of its own adapter: other lanes load from a
 //    zero block in the workspace instead (a direct load cannot mask).  An M
@@ -54,19 +58,26 @@ constexpr int kCons = 4;                       // consumer waves
 constexpr int kNTW = 4;                        // 16-column tiles per consumer
 constexpr int kSlabCols = kCons * kNTW * 16;   // 256 columns per block
 constexpr int kThreadsW = 2 * kCons * kWave;   // consumers + producers
-constexpr int kStages = 5;                     // K chunks resident in LDS
-constexpr int kAStageBytes = kWRows * 64;      // 176 rows x 32 bf16
-constexpr int kBStageBytes = kCons * kNTW * 1024;  // 16 MFMA B fragments
-constexpr int kStageBytes = kAStageBytes + kBStageBytes;
-constexpr int kAPerProd = (kWMT + kCons - 1) / kCons;  // A loads per producer: 3
+constexpr int kWStages = 5;                    // weight chunks (32 K each) resident in LDS
+constexpr int kXStages = 3;                    // activation chunk pairs (64 K each) resident
+constexpr int kXRowBytes = 128;                // a row's share of a chunk pair: one cache line
+constexpr int kXStageBytes = kWRows * kXRowBytes;  // 176 rows x 64 bf16
+constexpr int kWStageBytes = kCons * kNTW * 1024;  // 16 MFMA B fragments
+constexpr int kAPerProd = (kWMT + kCons - 1) / kCons;  // M tiles per producer: 3
 constexpr int kWideCUs = 256;                  // MI355X compute units (one block each)
+
+// physical 16-byte slot of logical piece p (0..7) of activation row `row`
+// in a chunk-pair stage: p ^ xline_swizzle(row)
+__device__ __forceinline__ int xline_swizzle(int row) { return (row >> 1) & 7; }
 
 template <bool kGated>
 __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs a)
 {
-    __shared__ __align__(1024) unsigned char smem[kStages * kStageBytes];
-    // LDS byte address of smem, for the direct loads (M0)
-    const uint32_t smem_lds = lds_address(smem);
+    __shared__ __align__(1024) unsigned char xsm[kXStages * kXStageBytes];
+    __shared__ __align__(1024) unsigned char wsm[kWStages * kWStageBytes];
+    // LDS byte addresses of the two rings, for the direct loads (M0)
+    const uint32_t xsm_lds = lds_address(xsm);
+    const uint32_t wsm_lds = lds_address(wsm);
     __shared__ int row_x[kWRows];
     __shared__ int row_src[kWRows];
     __shared__ int row_adapter[kWRows];
@@ -104,12 +115,16 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
     const bool lora = a.S != nullptr && a.L > 0 && a.r > 0;
     const int n_ext = lora ? (a.L * a.rp + 31) >> 5 : 0;
     const int nv = KC + n_ext;  // main K chunks, then the LoRA expand chunks
-    // The block's chunk sequence q = 0 .. nq - 1 runs the slabs in turn:
-    // slab slab0 + q / nv, chunk q % nv.  Every chunk carries the same loads
+    // Chunks go in pairs (the activation rows of a pair are one 128-byte line
+    // per row), so a slab's sequence is padded to an even length nv2 (KC is
+    // even; a padding chunk reads zeros and multiplies nothing).  The block's
+    // chunk sequence q = 0 .. nq - 1 runs the slabs in turn: slab slab0 +
+    // q / nv2, chunk q % nv2.  Chunks of equal parity carry the same loads
     // (the rows are the same for all slabs), so the producers' wait counts
     // do not change across slabs, and they run on into the next slab while
     // the consumers finish the previous one.
-    const int nq = n_sl * nv;
+    const int nv2 = (nv + 1) & ~1;
+    const int nq = n_sl * nv2;
 
     // rows of this tile: slot, source row, adapter (rows past the tile
     // repeat the last row and carry no adapter)
@@ -139,39 +154,65 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
 
     if (wave >= kCons) {
         // ------------------------------------------------------------ producer
-        // A loads: M tiles j = g + 4 i that exist.  Lane `lane` of the load of
-        // M tile j fills physical row 16 j + lane / 4, physical quarter
-        // lane % 4, which holds logical quarter (lane % 4) ^ swizzle(row).
+        // Activation loads, once per chunk pair: M tiles j = g + 4 i that
+        // exist, two loads each (rows 16 j .. 16 j + 7, then + 8 .. + 15).
+        // Lane `lane` of a load fills row 16 j + 8 u + lane / 8, physical
+        // slot lane % 8, which holds logical piece (lane % 8) ^ swizzle(row):
+        // eight K values of the pair (pieces 0-3: the even chunk, 4-7: the
+        // odd one).
         const int n_a = max(0, min(kAPerProd, (n_mt - g + kCons - 1) / kCons));
-        const uint16_t *a_src[kAPerProd];
-        int a_x[kAPerProd], a_ad[kAPerProd], a_q[kAPerProd];
+        const uint16_t *a_src[kAPerProd][2];
+        int a_x[kAPerProd][2], a_ad[kAPerProd][2], a_p[kAPerProd][2];
 #pragma unroll
         for (int i = 0; i < kAPerProd; ++i) {
-            const int j = min(g + kCons * i, kWMT - 1);
-            const int pr = 16 * j + (lane >> 2);
-            const int q = (lane & 3) ^ act_swizzle(pr);
-            a_src[i] = a.X + (size_t)row_src[pr] * a.K + q * 8;
-            a_x[i] = row_x[pr];
-            a_ad[i] = row_adapter[pr];
-            a_q[i] = q;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int j = min(g + kCons * i, kWMT - 1);
+                const int pr = 16 * j + 8 * u + (lane >> 3);
+                const int p = (lane & 7) ^ xline_swizzle(pr);
+                a_src[i][u] = a.X + (size_t)row_src[pr] * a.K + p * 8;
+                a_x[i][u] = row_x[pr];
+                a_ad[i][u] = row_adapter[pr];
+                a_p[i][u] = p;
+            }
         }
         // B loads: the four fragments of weight slab s64 (contiguous 4 KiB
         // per chunk), or the LoRA B columns of its four 16-column tiles
         const uint16_t *zeros = a.zeros;
         const size_t slab_elems = (size_t)KC * 4 * 512;  // one packed 64-column slab
 
-        // issue every load of chunk vc of the block's slab si into stage st;
-        // `lean`: a main K chunk (vc < KC)
-        auto issue = [&](auto na, auto lean, int si, int vc, int st) __attribute__((always_inline)) {
+        // the activation rows of the chunk pair (vc, vc + 1), vc even, into
+        // pair stage xst; main K pairs read hidden / act rows, expand pairs
+        // keep each row's own adapter block (others, and padding past the
+        // last adapter, read the zero block)
+        auto issue_x = [&](auto na, int vc, int xst) __attribute__((always_inline)) {
             constexpr int NA = decltype(na)::value;
+            const uint32_t sx = xsm_lds + (uint32_t)(xst * kXStageBytes);
+#pragma unroll
+            for (int i = 0; i < NA; ++i) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const uint32_t dst = sx + (g + kCons * i) * 2048 + u * 1024;
+                    if (vc < KC) {
+                        load_lds16(a_src[i][u] + vc * 32, dst);
+                    } else {
+                        const int gq = (vc - KC) * 32 + a_p[i][u] * 8;
+                        const int aid = gq / a.rp;
+                        const uint16_t *p = a_ad[i][u] == aid
+                                                ? a.S + (size_t)a_x[i][u] * a.rp + (gq - aid * a.rp)
+                                                : zeros;
+                        load_lds16(p, dst);
+                    }
+                }
+            }
+        };
+        // the weight (or LoRA B) fragments of chunk vc of slab si into weight
+        // stage wst
+        auto issue_w = [&](int si, int vc, int wst) __attribute__((always_inline)) {
             const int s64 = (slab0 + si) * kCons + g;
             const bool has_cols = s64 < NS64;
-            const uint32_t sa = smem_lds + (uint32_t)(st * kStageBytes);
-            const uint32_t sb = sa + kAStageBytes + g * kNTW * 1024;
-            if (decltype(lean)::value) {
-#pragma unroll
-                for (int i = 0; i < NA; ++i)
-                    load_lds16(a_src[i] + vc * 32, sa + (g + kCons * i) * 1024);
+            const uint32_t sb = wsm_lds + (uint32_t)(wst * kWStageBytes) + g * kNTW * 1024;
+            if (vc < KC) {
 #pragma unroll
                 for (int t = 0; t < kNTW; ++t) {
                     if (has_cols)  // weights are read once: streaming hint
@@ -183,16 +224,7 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
                 }
                 return;
             }
-            const int c = vc - KC;
-#pragma unroll
-            for (int i = 0; i < NA; ++i) {
-                const int gq = c * 32 + a_q[i] * 8;
-                const int aid = gq / a.rp;
-                const uint16_t *p =
-                    a_ad[i] == aid ? a.S + (size_t)a_x[i] * a.rp + (gq - aid * a.rp) : zeros;
-                load_lds16(p, sa + (g + kCons * i) * 1024);
-            }
-            const int gq = c * 32 + (lane >> 4) * 8;
+            const int gq = (vc - KC) * 32 + (lane >> 4) * 8;
             const int aid = gq / a.rp;
             const int q0 = gq - aid * a.rp;
 #pragma unroll
@@ -208,33 +240,37 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
                 load_lds16(p, sb + t * 1024);
             }
         };
-        // The stage of the block's chunk q is q % kStages.  Chunks 0 .. S - 2
-        // go out first; after the barrier of chunk q, chunk q + S - 1 goes
-        // into the stage chunk q - 1 has left.  Past the last chunk the last
-        // one is issued again, so the loads per chunk never change: chunk q
-        // has landed once only the (S - 2) chunks issued after it can be
-        // outstanding.  (si, vc): the next chunk to issue.
+        // Chunk q's weights live in weight stage q % kWStages, its pair's
+        // activation rows in pair stage (q / 2) % kXStages; an even chunk
+        // also issues its pair's activation rows.  Chunks 0 .. kWStages - 2
+        // go out first; after the barrier of chunk q, chunk q + kWStages - 1
+        // goes out into the stages chunk q - 1 (and, for an even chunk, the
+        // pair before chunk q's) has left.  Past the last chunk the last pair
+        // is issued again by parity, so the loads per chunk never change and
+        // chunk q has landed once only the loads of the three chunks issued
+        // after it can be outstanding: 3 kNTW + 2 NA of them after an even
+        // chunk, 3 kNTW + 4 NA after an odd one.  (qn: the next chunk.)
         auto run = [&](auto na) __attribute__((always_inline)) {
-            constexpr int kLoads = decltype(na)::value + kNTW;
-            int si = 0, vc = 0, st = 0;
+            constexpr int NA = decltype(na)::value;
+            constexpr int kAfterEven = 3 * kNTW + 2 * NA;
+            constexpr int kAfterOdd = 3 * kNTW + 4 * NA;
+            int qn = 0;
             auto issue_next = [&]() __attribute__((always_inline)) {
-                const bool past = si >= n_sl;
-                const int s_i = past ? n_sl - 1 : si;
-                const int v_i = past ? nv - 1 : vc;
-                if (v_i < KC)
-                    issue(na, std::true_type{}, s_i, v_i, st);
-                else
-                    issue(na, std::false_type{}, s_i, v_i, st);
-                st = st == kStages - 1 ? 0 : st + 1;
-                if (!past && ++vc == nv) {
-                    vc = 0;
-                    ++si;
-                }
+                const bool past = qn >= nq;
+                const int si = past ? n_sl - 1 : qn / nv2;
+                const int vc = past ? nv2 - 2 + (qn & 1) : qn - (qn / nv2) * nv2;
+                if ((qn & 1) == 0)
+                    issue_x(na, vc, (qn >> 1) % kXStages);
+                issue_w(si, vc, qn % kWStages);
+                ++qn;
             };
-            for (int d = 0; d < kStages - 1; ++d)
+            for (int d = 0; d < kWStages - 1; ++d)
                 issue_next();
             for (int q = 0; q < nq; ++q) {
-                dma_wait_barrier<(kStages - 2) * kLoads>();
+                if (q & 1)
+                    dma_wait_barrier<kAfterOdd>();
+                else
+                    dma_wait_barrier<kAfterEven>();
                 issue_next();
             }
             dma_drain();  // no direct load may land after the block's LDS is released
@@ -262,14 +298,17 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
         return __builtin_amdgcn_readfirstlane(t & main_tiles);
     };
 
-    int st = 0;  // stage of the block's next chunk, as in the producers
+    int q = 0;  // the block's chunk counter, as in the producers
     for (int si = 0; si < n_sl; ++si) {
         // per-lane offsets are recomputed in every slab from an opaque copy
         // of the lane index: hoisted out of the loop they would stay live
         // beside the 176 accumulator registers and spill
         int ln = lane;
         asm volatile("" : "+v"(ln));
-        const int a_lane_off = (ln & 15) * 64 + (((ln >> 4) ^ act_swizzle(ln & 15)) * 16);
+        // fragment row ln % 16 of an M tile, K piece ln / 16 of the even
+        // chunk (4 + ln / 16 of the odd one), at its swizzled slot
+        const int a_off0 = (ln & 15) * kXRowBytes + ((((ln >> 4)) ^ xline_swizzle(ln & 15)) << 4);
+        const int a_off1 = (ln & 15) * kXRowBytes + (((4 + (ln >> 4)) ^ xline_swizzle(ln & 15)) << 4);
         const int s64 = (slab0 + si) * kCons + g;
         const bool has_cols = s64 < NS64;
         f32x4 acc[kWMT][kNTW];
@@ -282,23 +321,24 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
         const uint32_t main_tiles =
             __builtin_amdgcn_readfirstlane(has_cols ? (1u << n_mt) - 1u : 0u);
 
-        // multiply the chunk in stage st for the M tiles in `tiles`; A
-        // fragments are read two M tiles ahead of their MFMAs (a ring of three)
-        auto compute = [&](int stage, uint32_t tiles) __attribute__((always_inline)) {
-            const unsigned char *sa = smem + stage * kStageBytes;
-            const unsigned char *sb = sa + kAStageBytes + g * kNTW * 1024 + ln * 16;
+        // multiply chunk q for the M tiles in `tiles`; A fragments are read
+        // two M tiles ahead of their MFMAs (a ring of three)
+        auto compute = [&](int qq, uint32_t tiles) __attribute__((always_inline)) {
+            const unsigned char *sa = xsm + ((qq >> 1) % kXStages) * kXStageBytes +
+                                      ((qq & 1) ? a_off1 : a_off0);
+            const unsigned char *sb =
+                wsm + (qq % kWStages) * kWStageBytes + g * kNTW * 1024 + ln * 16;
             u32x4 b[kNTW];
 #pragma unroll
             for (int t = 0; t < kNTW; ++t)
                 b[t] = *reinterpret_cast<const u32x4 *>(sb + t * 1024);
             u32x4 av[3];
-            av[0] = *reinterpret_cast<const u32x4 *>(sa + a_lane_off);
-            av[1] = *reinterpret_cast<const u32x4 *>(sa + 1024 + a_lane_off);
+            av[0] = *reinterpret_cast<const u32x4 *>(sa);
+            av[1] = *reinterpret_cast<const u32x4 *>(sa + 2048);
 #pragma unroll
             for (int m = 0; m < kWMT; ++m) {
                 if (m + 2 < kWMT)  // rows past the tile: read, never used
-                    av[(m + 2) % 3] =
-                        *reinterpret_cast<const u32x4 *>(sa + (m + 2) * 1024 + a_lane_off);
+                    av[(m + 2) % 3] = *reinterpret_cast<const u32x4 *>(sa + (m + 2) * 2048);
                 if (tiles & (1u << m)) {
 #pragma unroll
                     for (int t = 0; t < kNTW; ++t)
@@ -307,10 +347,10 @@ __global__ __launch_bounds__(kThreadsW, 1) void expert_gemm_wide_kernel(GemmArgs
             }
         };
 
-        for (int vc = 0; vc < nv; ++vc) {
+        for (int vc = 0; vc < nv2; ++vc, ++q) {
             dma_wait_barrier<63>();  // the chunk has landed; this wave's reads of the previous one are done
-            compute(st, vc < KC ? main_tiles : ext_tiles(vc, main_tiles));
-            st = st == kStages - 1 ? 0 : st + 1;
+            if (vc < nv)  // uniform: the padding chunk multiplies nothing
+                compute(q, vc < KC ? main_tiles : ext_tiles(vc, main_tiles));
         }
 
         // Epilogue of this slab (the producers meanwhile fill the stages with

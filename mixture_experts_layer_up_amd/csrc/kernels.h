@@ -40,8 +40,9 @@ struct PermuteArgs {
 
 // The permute cuts the slots into blocks of kPermuteSlotsPerBlock; with more
 // than one block its count kernel writes every block's histogram of both key
-// types to the workspace, rows padded to a multiple of 4 keys:
-// G * (round4(E_l) + round4(L * E_l)) int32.
+// types to the workspace, rows padded to a multiple of 4 keys, followed by
+// one totals row per key type: (G + 1) * (round4(E_l) + round4(L * E_l))
+// int32.
 constexpr int kPermuteSlotsPerBlock = 1024;
 
 inline int permute_blocks(int n)
@@ -49,11 +50,12 @@ inline int permute_blocks(int n)
     return n <= 0 ? 1 : (n + kPermuteSlotsPerBlock - 1) / kPermuteSlotsPerBlock;
 }
 
+inline size_t round4_host(size_t v) { return (v + 3) / 4 * 4; }
+
 inline size_t permute_scratch_bytes(int n, int E_l, int L)
 {
     const int G = permute_blocks(n);
-    auto round4 = [](size_t v) { return (v + 3) / 4 * 4; };
-    return G > 1 ? (size_t)G * (round4(E_l) + round4((size_t)L * E_l)) * 4 : 0;
+    return G > 1 ? ((size_t)G + 1) * (round4_host(E_l) + round4_host((size_t)L * E_l)) * 4 : 0;
 }
 
 // A small all-zero region of the workspace, rewritten by every permute

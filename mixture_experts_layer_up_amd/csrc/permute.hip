@@ -16,9 +16,11 @@
 // Two key types run side by side: blockIdx.y = 0 sorts slots by local expert,
 // blockIdx.y = 1 by virtual expert (adapter * E_l + local expert).  The slots
 // are cut into G = ceil(n / kPermuteSlotsPerBlock) consecutive blocks.  With G > 1 a
-// count kernel first writes every block's histogram to the workspace; the
-// rank kernel's blocks then each read the histograms, scan the totals into
-// the offsets (every block the same, redundantly) and rank their own slots:
+// count kernel first writes every block's histogram to the workspace; with
+// more than 16 blocks a scan kernel then turns them into, per key, the slots
+// in earlier blocks and the key's total (so the work stays linear in G);
+// the rank kernel's blocks then each scan the totals into the
+// offsets (every block the same, redundantly) and rank their own slots:
 // position = offset of the key + slots of the key in earlier blocks + in
 // earlier waves of the block + in earlier 64-slot groups of the wave + lower
 // lanes of the group with the same key.  With G == 1 the rank kernel's own
@@ -39,6 +41,7 @@ constexpr int kIters = kPermuteSlotsPerBlock / kThreads;  // 64-slot groups per 
 constexpr int kMaxKeys = 8192;                            // local experts, or adapters * local experts
 constexpr int kMaxExperts = 1024;
 constexpr int kFusedKeys = 1024;                          // keys of the permute fused with the shrink
+constexpr int kScanMinBlocks = 17;  // slot blocks from which the histograms are scanned first
 
 // key of a slot from its expert id and its token's adapter l (-1: none)
 __device__ __forceinline__ int key_from(const PermuteArgs &a, bool by_segment, int id, int l)
@@ -164,6 +167,38 @@ __global__ __launch_bounds__(kThreads) void permute_count_kernel(PermuteArgs a)
         dst[j] = j < NK ? hist[j] : 0;
 }
 
+// With several slot blocks: per key, the exclusive prefix over the blocks of
+// their histograms (in place: row g becomes the key's slots in blocks
+// 0 .. g - 1) and the key's total (the totals row after both key types'
+// rows).  One thread per key, blocks in order; every block's histogram is
+// read once, so the work is linear in G * keys.
+__global__ __launch_bounds__(kThreads) void permute_scan_kernel(PermuteArgs a)
+{
+    const bool by_segment = blockIdx.y == 1;
+    const int NKs = round4(by_segment ? a.L * a.E_l : a.E_l);
+    const int j = blockIdx.x * kThreads + threadIdx.x;
+    if (j >= NKs)
+        return;
+    int32_t *rows = a.block_counts + (by_segment ? (size_t)a.G * round4(a.E_l) : 0);
+    int32_t *totals = a.block_counts + (size_t)a.G * (round4(a.E_l) + round4(a.L * a.E_l)) +
+                      (by_segment ? round4(a.E_l) : 0);
+    int run = 0;
+    for (int g0 = 0; g0 < a.G; g0 += 16) {
+        int c[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)  // all loads of a batch in flight together
+            c[u] = g0 + u < a.G ? rows[(size_t)(g0 + u) * NKs + j] : 0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            if (g0 + u < a.G) {
+                rows[(size_t)(g0 + u) * NKs + j] = run;
+                run += c[u];
+            }
+        }
+    }
+    totals[j] = run;
+}
+
 // The rank pass of slot block g for one key type.  kKeys bounds the keys
 // (E_l, or L * E_l) and kExperts the local experts: they size the LDS tables.
 template <int kKeys, int kExperts>
@@ -216,36 +251,42 @@ __device__ __forceinline__ void permute_rank_body(const PermuteArgs &a, bool by_
 
     // 2. totals per key, their exclusive scan (the offsets), and each wave's
     // first position per key.  Keys in rows of 4 * kThreads, four consecutive
-    // keys per thread, so that the other blocks' histograms (written by the
-    // count kernel, mostly in other XCDs' caches) come in as int4 loads, 16
-    // blocks' rows per batch, all in flight together.
+    // keys per thread.  With up to 16 slot blocks every block reads all the
+    // blocks' histogram rows (int4 loads, all in flight together); with more,
+    // the scan kernel has turned them into, per key, the slots in earlier
+    // blocks (row g) and the key's total (the totals row): two int4 loads per
+    // thread.
     const int NKs = round4(NK);
     const int32_t *counts = a.block_counts + (by_segment ? (size_t)G * round4(a.E_l) : 0);
+    const int32_t *totals = a.block_counts + (size_t)G * (round4(a.E_l) + round4(a.L * a.E_l)) +
+                            (by_segment ? round4(a.E_l) : 0);
     int carry = 0;
     for (int j0 = 0; j0 < NK; j0 += 4 * kThreads) {
         const int jb = j0 + 4 * tid;
-        int before[4] = {0, 0, 0, 0}, after[4] = {0, 0, 0, 0};
-        if (G > 1 && jb < NK) {
-            for (int q0 = 0; q0 < G; q0 += 16) {
-                int4 c[16];
+        int before[4] = {0, 0, 0, 0}, all[4] = {0, 0, 0, 0};
+        if (G > kScanMinBlocks - 1 && jb < NK) {
+            const int4 b = *reinterpret_cast<const int4 *>(counts + (size_t)g * NKs + jb);
+            const int4 t = *reinterpret_cast<const int4 *>(totals + jb);
+            before[0] = b.x, before[1] = b.y, before[2] = b.z, before[3] = b.w;
+            all[0] = t.x, all[1] = t.y, all[2] = t.z, all[3] = t.w;
+        } else if (G > 1 && jb < NK) {
+            // few blocks: read every block's histogram row directly, all in
+            // flight together (rows past G are clamped and not counted)
+            int4 c[kScanMinBlocks - 1];
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {  // clamped rows: in bounds, counted only if real
-                    const int q = min(q0 + u, G - 1);
-                    c[u] = *reinterpret_cast<const int4 *>(counts + (size_t)q * NKs + jb);
-                }
+            for (int u = 0; u < kScanMinBlocks - 1; ++u)
+                c[u] = *reinterpret_cast<const int4 *>(counts + (size_t)min(u, G - 1) * NKs + jb);
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const int q = q0 + u;
-                    const bool lo = q < g, hi = q > g && q < G;
-                    before[0] += lo ? c[u].x : 0;
-                    before[1] += lo ? c[u].y : 0;
-                    before[2] += lo ? c[u].z : 0;
-                    before[3] += lo ? c[u].w : 0;
-                    after[0] += hi ? c[u].x : 0;
-                    after[1] += hi ? c[u].y : 0;
-                    after[2] += hi ? c[u].z : 0;
-                    after[3] += hi ? c[u].w : 0;
-                }
+            for (int u = 0; u < kScanMinBlocks - 1; ++u) {
+                const bool lo = u < g, in = u < G;
+                before[0] += lo ? c[u].x : 0;
+                before[1] += lo ? c[u].y : 0;
+                before[2] += lo ? c[u].z : 0;
+                before[3] += lo ? c[u].w : 0;
+                all[0] += in ? c[u].x : 0;
+                all[1] += in ? c[u].y : 0;
+                all[2] += in ? c[u].z : 0;
+                all[3] += in ? c[u].w : 0;
             }
         }
         int wc[4][kWaves], total[4];
@@ -260,7 +301,7 @@ __device__ __forceinline__ void permute_rank_body(const PermuteArgs &a, bool by_
                 wc[m][w] = valid ? table[w * NK + j] : 0;
                 in_block += wc[m][w];
             }
-            total[m] = valid ? before[m] + in_block + after[m] : 0;
+            total[m] = valid ? (G > 1 ? all[m] : in_block) : 0;
             mine += total[m];
         }
         int row_total;
@@ -478,6 +519,11 @@ hipError_t launch_permute(const PermuteArgs &a, hipStream_t s)
     const int G = a.G;
     if (G > 1)
         hipLaunchKernelGGL(permute_count_kernel, dim3(G, 2), dim3(kThreads), 0, s, a);
+    if (G >= kScanMinBlocks) {
+        const int keys = round4_host(a.E_l > a.L * a.E_l ? a.E_l : a.L * a.E_l);
+        hipLaunchKernelGGL(permute_scan_kernel, dim3((keys + kThreads - 1) / kThreads, 2),
+                           dim3(kThreads), 0, s, a);
+    }
     hipLaunchKernelGGL(permute_rank_kernel, dim3(G, 2), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }

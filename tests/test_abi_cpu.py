@@ -227,18 +227,18 @@ def test_routing_method_validation(lib):
 
 def test_route_workspace_size_and_validation(lib):
     """moe_lora_route needs workspace only for more than one permute block
-    (1024 slots): G = ceil(T * k / 1024) histograms of E_l and L * E_l counts,
-    each row padded to a multiple of 4."""
+    (1024 slots): G = ceil(T * k / 1024) histograms of E_l and L * E_l counts
+    and one totals row of each, each row padded to a multiple of 4."""
     small = binding.make_shape(CONFIGS["decode64"])          # 512 slots
     assert lib.moe_lora_route_workspace_size(ctypes.byref(small)) == 0
     cfg = CONFIGS["prefill"]                                 # 16384 slots
     big = binding.make_shape(cfg)
     G = cfg.num_tokens * cfg.top_k // 1024
     E_l, L = cfg.local_num_experts, cfg.num_loras
-    need = G * (E_l + L * E_l) * 4
+    need = (G + 1) * (E_l + L * E_l) * 4
     assert lib.moe_lora_route_workspace_size(ctypes.byref(big)) == need
     odd = binding.make_shape(cfg.replace(local_num_experts=5, num_experts=128, num_loras=3))
-    assert lib.moe_lora_route_workspace_size(ctypes.byref(odd)) == G * (8 + 16) * 4
+    assert lib.moe_lora_route_workspace_size(ctypes.byref(odd)) == (G + 1) * (8 + 16) * 4
     # the forward workspace holds it too
     assert binding.workspace_size(big) > need
     rs = _routing_fake()

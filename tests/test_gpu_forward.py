@@ -126,6 +126,25 @@ def test_prefill_all_rows():
         assert np.abs(got[a * 512:(a + 1) * 512]).max() > 0.1 * np.abs(ref).max()
 
 
+def test_prefill_4096_tokens_all_rows():
+    """A 4096-token prefill (32,768 slots): 207 .. 303 rows per expert, so two
+    176-row tiles per expert in the many-row GEMMs (the second ragged), more
+    than 16 permute slot blocks (the histogram scan), and (adapter, expert)
+    segments around the many-row shrink's 64-row pass, some taking two
+    passes.  Every row against the oracle."""
+    cfg = CONFIGS["prefill"].replace(name="prefill4096", num_tokens=4096, run_length=1024,
+                                     seed=57)
+    announce("forward prefill4096 (all rows)")
+    inp = make_inputs(cfg)
+    got, r = run_forward(cfg, inp, routing=True)
+    ids, _ = oracle.route(inp["logits"], cfg.top_k)
+    np.testing.assert_array_equal(r["topk_ids"], ids)
+    perm = oracle.permute(ids, inp["mapping"], 128, 0, 128, 4)
+    for name in perm:
+        np.testing.assert_array_equal(r[name], perm[name], err_msg=name)
+    _compare(cfg, inp, got)
+
+
 @pytest.mark.parametrize("cfg", [MID, MID_R64, MID_EP, BIG_ROWS, TINY_AMP, WIDE, WIDE_R8,
                                  WIDE_H128, SHRINK_R20, SHRINK_MT2, SHRINK_FEW2, SHRINK_FEW3,
                                  FUSED_FULL, SPLIT_FEW, MANY_PAIRS, SLAB_GROUPS, PAIRS_1024,

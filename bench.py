@@ -554,7 +554,12 @@ def main():
     ap.add_argument("--prefill-leg", type=int, default=1,
                     help="with the default decode64 workload, also time the T=2048 prefill "
                          "layer and report it under `prefill` (1 = yes)")
-    ap.add_argument("--prefill-steps", type=int, default=50)
+    ap.add_argument("--prefill-steps", type=int, default=100)
+    ap.add_argument("--prefill-warmup", type=int, default=300,
+                    help="untimed prefill steps first: after the decode leg and the CPU "
+                         "baseline the GPU has idled for tens of seconds, and prefill steps "
+                         "only reach their steady time after ~100 (5 warm-up steps measured "
+                         "~8% slow)")
     ap.add_argument("--lora-layout", default="per_expert", choices=("per_expert", "shared_outer"),
                     help="LoRA stack layout (shared_outer: A_gu and B_dn one set per adapter)")
     ap.add_argument("--finalize", default="fused", choices=("fused", "external"),
@@ -634,10 +639,11 @@ def main():
             and args.finalize == "fused" and not args.routing_method and not args.routing_bias_sigma:
         import torch
         torch.cuda.empty_cache()
-        p = measure(args, "prefill", args.prefill_steps, max(2, args.warmup // 4),
+        p = measure(args, "prefill", args.prefill_steps, args.prefill_warmup,
                     min(args.cold_steps, 10), bool(args.graph), bool(args.two_stream))
         result["prefill"] = {
             "value": p["value"], "unit": "tokens/s", "steps": args.prefill_steps,
+            "warmup": args.prefill_warmup,
             "ms_per_step": p["ms_per_step"], "config": p["config"], "roofline": p["roofline"],
             "layer": p["layer"], "stages_us": p["stages_us"], "graph_replay": p["graph_replay"],
             "cold_cache": p["cold_cache"],

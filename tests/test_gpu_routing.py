@@ -63,7 +63,9 @@ def test_routing_bit_exact_on_layer_configs(name):
     # the largest segment key space (L * E_l = 8192)
     (1500, 40, 3, 3, 13, 3), (2000, 1024, 8, 0, 1024, 8),
     # 128 permute blocks (131,072 slots): the histogram scan over many blocks
-    (16384, 128, 8, 0, 128, 4)])
+    (16384, 128, 8, 0, 128, 4),
+    # 21 blocks with 13 experts and 39 segment keys: the scan over padded rows
+    (3000, 40, 7, 3, 13, 3)])
 def test_routing_edge_shapes(T, E, k, off, E_l, L):
     announce(f"routing edge T={T} E={E} k={k} off={off} E_l={E_l} L={L}")
     cfg = CONFIGS["tiny"].replace(num_tokens=T, num_experts=E, top_k=k, local_expert_offset=off,

@@ -168,9 +168,12 @@ def test_small_shapes_and_lora_delta(cfg):
     assert err <= bound, f"{cfg.name}: LoRA delta err {err:.3e} > {bound:.3e}"
 
 
-def test_no_adapter_paths_equal_base_bitwise():
-    announce("forward: no-adapter paths")
-    cfg = MID
+@pytest.mark.parametrize("cfg", [MID, WIDE], ids=lambda c: c.name)
+def test_no_adapter_paths_equal_base_bitwise(cfg):
+    """Every way of giving no token an adapter (no adapters, all -1, no
+    mapping, out-of-range ids, zero B, rank 0) yields the base layer bit for
+    bit, on the few-row and the many-row kernels."""
+    announce(f"forward: no-adapter paths {cfg.name}")
     inp = make_inputs(cfg)
     base, _ = run_forward(cfg.replace(num_loras=0), inp)
     none_mapped, _ = run_forward(cfg, inp, mapping=np.full(cfg.num_tokens, -1, np.int32))
@@ -187,6 +190,23 @@ def test_no_adapter_paths_equal_base_bitwise():
     r0, _ = run_forward(cfg.replace(rank_gate_up=0, rank_down=0), inp)
     np.testing.assert_array_equal(r0, base)
     _compare(cfg.replace(num_loras=0), inp, base)
+
+
+@pytest.mark.parametrize("cfg", [
+    MID.replace(name="gate_up_lora_only", rank_down=0, seed=61),
+    MID.replace(name="down_lora_only", rank_gate_up=0, seed=62),
+    WIDE.replace(name="wide_down_lora_only", rank_gate_up=0, seed=63),
+    WIDE.replace(name="wide_gate_up_lora_only", rank_down=0, seed=64)], ids=lambda c: c.name)
+def test_lora_on_one_projection_only(cfg):
+    """Rank 0 on one projection and not the other: that projection takes the
+    no-LoRA path (no shrink, no expand chunks) while the other keeps its
+    delta, on the few-row and the many-row kernels."""
+    announce(f"forward {cfg.name}")
+    inp = make_inputs(cfg)
+    got, _ = run_forward(cfg, inp)
+    ref = _compare(cfg, inp, got)
+    base = oracle.forward(cfg.replace(num_loras=0), inp)
+    assert np.abs(ref - base).max() > 10 * tol(base)  # the remaining delta is visible
 
 
 @pytest.mark.parametrize("cfg", [

@@ -139,6 +139,7 @@ def algorithmic_cost(cfg, ids, mapping):
 PROFILES = os.path.join(ROOT, "profiles")
 GEMM_SOURCES = ["mixture_experts_layer_up_amd/csrc/expert_gemm.hip",
                 "mixture_experts_layer_up_amd/csrc/expert_gemm_wide.hip",
+                "mixture_experts_layer_up_amd/csrc/gemm_index.h",
                 "mixture_experts_layer_up_amd/csrc/mfma_pipeline.h",
                 "mixture_experts_layer_up_amd/csrc/lora_shrink_rows.h",
                 "mixture_experts_layer_up_amd/csrc/device_common.h",
@@ -151,11 +152,18 @@ DOMINANT = {"decode": "expert_gemm_kernel<1, 1, true, true>", "prefill": "expert
 
 
 def gemm_source_hash() -> str:
+    """Hash of the GEMM kernels' code: their sources with comments and blank
+    lines removed, so that a comment edit keeps the committed counters."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in GEMM_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 

@@ -248,7 +248,7 @@ int gemm_tile_rows(int n_slots, int E_l, int H, int I, int r_gu, int r_dn)
     // the wide kernel once experts average 32 or more rows
     if (n_slots < 32 * E_l || !gemm_wide_supported(H, I, r_gu, r_dn))
         return kDecodeTileRows;
-    // Every wide work item streams a whole 128-column weight slab whatever
+    // Every wide work item streams whole 256-column weight slabs whatever
     // its rows, so a launch costs about ceil(items / resident blocks) item
     // times: an expert split over two tiles adds a nearly empty item per
     // slab, and a few of those start a whole extra round.  Tiles therefore

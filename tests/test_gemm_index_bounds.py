@@ -113,6 +113,10 @@ SHAPES = [
     ("decode64_gate_up", 2048, 1536, 1, 768, 4, 16, 128, 0),
     ("decode64_down", 768, 2048, 0, 768, 4, 16, 128, 0),
     ("rank_256_one_adapter", 128, 128, 1, 64, 1, 256, 2, 0),
+    # the largest rank on both projections, two adapters (the forward's
+    # rank-256 parity case): 16 expand chunks per adapter
+    ("rank_256_gate_up", 256, 256, 1, 128, 2, 256, 8, 0),
+    ("rank_256_down", 128, 256, 0, 128, 2, 256, 8, 0),
 ]
 
 

@@ -89,6 +89,14 @@ SLAB_GROUPS = LayerConfig("slab_groups", 640, 640, 320, 128, 8, 0, 128, 3, 24, 2
 # loads): those waves run expand chunks only
 K64_R20 = LayerConfig("k64_r20", 37, 128, 64, 16, 4, 0, 16, 4, 20, 20, seed=49,
                       mapping="uniform", sigma_lora_a=0.2, sigma_lora_b=0.2)
+# the largest accepted rank (256): 16 expand chunks per adapter in the GEMMs
+# and 16 rank tiles in the few-row shrink; few rows per expert, then ~300
+# (the many-row GEMM beside the few-row shrink, several row passes per
+# segment; down rank 248: a last rank tile of 8)
+RANK_256 = LayerConfig("rank_256", 40, 256, 128, 8, 2, 0, 8, 2, 256, 256, seed=50,
+                       mapping="uniform", sigma_lora_a=0.05, sigma_lora_b=0.05)
+WIDE_RANK_256 = LayerConfig("wide_rank_256", 600, 256, 128, 4, 2, 0, 4, 2, 256, 248, seed=51,
+                            mapping="uniform", sigma_lora_a=0.05, sigma_lora_b=0.05)
 
 
 def _compare(cfg, inp, got, tokens=None, **kw):
@@ -148,7 +156,7 @@ def test_prefill_4096_tokens_all_rows():
 @pytest.mark.parametrize("cfg", [MID, MID_R64, MID_EP, BIG_ROWS, TINY_AMP, WIDE, WIDE_R8,
                                  WIDE_H128, SHRINK_R20, SHRINK_MT2, SHRINK_FEW2, SHRINK_FEW3,
                                  FUSED_FULL, SPLIT_FEW, MANY_PAIRS, SLAB_GROUPS, PAIRS_1024,
-                                 EXPERTS_1024, K64_R20],
+                                 EXPERTS_1024, K64_R20, RANK_256, WIDE_RANK_256],
                          ids=lambda c: c.name)
 def test_small_shapes_and_lora_delta(cfg):
     announce(f"forward {cfg.name}")

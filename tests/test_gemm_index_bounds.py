@@ -117,6 +117,11 @@ SHAPES = [
     # rank-256 parity case): 16 expand chunks per adapter
     ("rank_256_gate_up", 256, 256, 1, 128, 2, 256, 8, 0),
     ("rank_256_down", 128, 256, 0, 128, 2, 256, 8, 0),
+    # the largest accepted hidden and inter sizes (65536)
+    ("hidden_65536_gate_up", 65536, 64, 1, 32, 1, 8, 2, 0),
+    ("hidden_65536_down", 32, 65536, 0, 32, 1, 8, 2, 0),
+    ("inter_65536_gate_up", 64, 131072, 1, 65536, 1, 8, 1, 0),
+    ("inter_65536_down", 65536, 64, 0, 65536, 1, 8, 1, 0),
 ]
 
 

@@ -201,6 +201,21 @@ def test_no_adapter_paths_equal_base_bitwise(cfg):
 
 
 @pytest.mark.parametrize("cfg", [
+    LayerConfig("hidden_65536", 8, 65536, 32, 2, 1, 0, 2, 1, 8, 8, seed=52, mapping="uniform",
+                sigma_lora_a=0.05, sigma_lora_b=0.05),
+    LayerConfig("inter_65536", 8, 64, 65536, 1, 1, 0, 1, 1, 8, 8, seed=53, mapping="uniform",
+                sigma_lora_a=0.05, sigma_lora_b=0.05)], ids=lambda c: c.name)
+def test_largest_hidden_and_inter(cfg):
+    """The largest hidden and inter sizes the shape check accepts (65,536):
+    2,048 K chunks in one GEMM, 1,024 or 2,048 column slabs in the other, 32
+    column blocks in the finalize."""
+    announce(f"forward {cfg.name}")
+    inp = make_inputs(cfg)
+    got, _ = run_forward(cfg, inp)
+    _compare(cfg, inp, got)
+
+
+@pytest.mark.parametrize("cfg", [
     MID.replace(name="gate_up_lora_only", rank_down=0, seed=61),
     MID.replace(name="down_lora_only", rank_gate_up=0, seed=62),
     WIDE.replace(name="wide_down_lora_only", rank_gate_up=0, seed=63),

@@ -200,6 +200,27 @@ def test_no_adapter_paths_equal_base_bitwise(cfg):
     _compare(cfg.replace(num_loras=0), inp, base)
 
 
+@pytest.mark.parametrize("cfg,hot", [
+    (LayerConfig("skewed_many_rows", 300, 256, 128, 16, 2, 0, 16, 2, 16, 16, seed=54,
+                 mapping="uniform", sigma_lora_a=0.05, sigma_lora_b=0.05), (3, 7)),
+    (CONFIGS["decode64"].replace(name="skewed_decode64", seed=55),
+     (5, 17, 33, 64, 90, 101, 120, 127))], ids=lambda v: getattr(v, "name", "hot"))
+def test_all_tokens_on_few_experts(cfg, hot):
+    """Every token routed to the same k experts (their logits raised by 10):
+    those experts carry T rows each (several row tiles, long segments), all
+    the others none (no work items at all)."""
+    announce(f"forward {cfg.name}")
+    inp = dict(make_inputs(cfg))
+    logits = inp["logits"].copy()
+    logits[:, list(hot)] += 10.0
+    inp["logits"] = logits
+    got, r = run_forward(cfg, inp, routing=True)
+    counts = np.zeros(cfg.local_num_experts, np.int64)
+    counts[list(hot)] = cfg.num_tokens
+    np.testing.assert_array_equal(r["expert_counts"], counts)
+    _compare(cfg, inp, got)
+
+
 @pytest.mark.parametrize("cfg", [
     LayerConfig("hidden_65536", 8, 65536, 32, 2, 1, 0, 2, 1, 8, 8, seed=52, mapping="uniform",
                 sigma_lora_a=0.05, sigma_lora_b=0.05),

@@ -1,6 +1,7 @@
-"""The bench's algorithmic cost model (bytes and flops per layer call, from
-the actual routing), checked against a hand-counted case and against a
-slot-by-slot recount of the same definition.
+"""The bench's measurement arithmetic.  The algorithmic cost model (bytes and
+flops per layer call, from the actual routing) is checked against a
+hand-counted case and against a slot-by-slot recount of the same
+definition; the counter summaries against a synthetic profile.
 
 The definition (what the layer must move at least once): the gate_up and
 down weights of every local expert some slot uses, the LoRA stacks of every
@@ -78,3 +79,33 @@ def test_matches_slot_by_slot_recount(name, shared):
     b, f, P, n_e, n_p = _recount(cfg, ids, mapping)
     assert (c["bytes"], c["flops"], c["local_slots"], c["touched_experts"],
             c["touched_lora_pairs"]) == (b, f, P, n_e, n_p)
+
+
+def test_counter_summary_scaling_and_read_back(tmp_path, monkeypatch):
+    """FETCH_SIZE / WRITE_SIZE per dispatch are scaled by what the counters
+    read for a copy kernel of known size (here: a counter that reports half
+    the bytes read and all the bytes written), and the dominant kernel's
+    bytes come back as the bench's `traffic` while the kernel code is
+    unchanged."""
+    copy = "void at::native::vectorized_elementwise_kernel<8, at::native::neg_kernel_cuda(x)>(int)"
+    dom = "void moe_lora::(anonymous namespace)::expert_gemm_kernel<1, 1, true, true>(GemmArgs)"
+
+    def csv_file(name, rows):
+        p = tmp_path / name
+        p.write_text("Kernel_Name,Counter_Value\n" +
+                     "".join(f'"{k}",{v}\n' for k, v in rows))
+        return str(p)
+
+    fetch = csv_file("fetch.csv", [(copy, 128 * 1024), (dom, 1000.0), (dom, 1004.0), (dom, 990.0)])
+    write = csv_file("write.csv", [(copy, 256 * 1024), (dom, 50.0), (dom, 50.0), (dom, 50.0)])
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    out = tmp_path / "gemm_gate_up_swiglu_decode64_hbm_counters.md"
+    bench.summarize_counters(fetch, write, str(out), command="test", copy_mib=256,
+                             dominant=bench.DOMINANT["decode"])
+    text = out.read_text()
+    assert "FETCH_SIZE factor 2.0000, WRITE_SIZE factor 1.0000" in text
+    # median fetch 1000 KiB x 2, write 50 KiB x 1, in bytes
+    assert bench.traffic_from_profile("decode64") == (1000 * 2 + 50) * 1024
+    # a summary taken on other kernel code is not used
+    out.write_text(text.replace(bench.gemm_source_hash(), "0" * 16))
+    assert bench.traffic_from_profile("decode64") is None

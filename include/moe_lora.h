@@ -163,11 +163,13 @@ typedef struct moe_lora_routing {
  *                      gate, [I, 2I) up) in the packed layout written by
  *                      moe_lora_pack_weights; 16-byte aligned
  *   w2_packed          expert down weights [E_l, I, H], packed; 16-byte aligned
- *   lora_a_gate_up     bf16 [L, E_l, r_gu, H]   (shrink, 16-byte aligned;
- *                      [L, 1, r_gu, H] in the shared-outer layout)
- *   lora_b_gate_up     bf16 [L, E_l, 2I, r_gu]  (expand; 16-byte aligned
- *                      when r_gu % 8 == 0, else 2-byte)
- *   lora_a_down        bf16 [L, E_l, r_dn, I]
+ *   lora_a_gate_up     shrink stacks bf16 [L, E_l, r_gu, H] ([L, 1, r_gu, H]
+ *                      in the shared-outer layout) in the packed layout
+ *                      written by moe_lora_pack_lora_a; 16-byte aligned
+ *   lora_b_gate_up     bf16 [L, E_l, 2I, r_gu]  (expand, as given; 16-byte
+ *                      aligned when r_gu % 8 == 0, else 2-byte)
+ *   lora_a_down        shrink stacks bf16 [L, E_l, r_dn, I], packed by
+ *                      moe_lora_pack_lora_a; 16-byte aligned
  *   lora_b_down        bf16 [L, E_l, H, r_dn]   ([L, 1, H, r_dn] shared-outer)
  *   token_lora_mapping int32 [T], adapter of each token, -1 = none; NULL
  *                      means every token is -1
@@ -268,6 +270,30 @@ size_t moe_lora_packed_w2_bytes(const moe_lora_shape *shape);
  */
 int moe_lora_pack_weights(const moe_lora_shape *shape, const void *w13, const void *w2,
                           void *w13_packed, void *w2_packed, void *stream);
+
+/*
+ * One-time relayout of the LoRA A stacks (the shrink operands), done when
+ * adapters are loaded, like the expert weights' pack.  The pages' LoRA path
+ * keeps per-(adapter, expert) stacks addressed as virtual experts ("BF16
+ * support for the experimental_sgl_trtllm MoE-LoRA path", Flow section 2);
+ * only the order inside each stack changes here.  An r x K stack becomes
+ * ceil(K / 64) chunks of r x 64 values, the rank rows of one chunk
+ * contiguous:
+ *   packed[((s * C + k / 64) * r + q) * 64 + k % 64] = A[s][q][k],  C = ceil(K / 64),
+ * with zeros for K <= k < 64 C.  Stacks s run over [L, E_l] (gate_up in the
+ * shared-outer layout: [L]); K is H for gate_up and I for down.  The shrink
+ * reads a stack chunk by chunk with every rank row at once, so each chunk is
+ * one sequential run instead of r rows 2K bytes apart.
+ *   a_gate_up [L, E_l or 1, r_gu, H] -> a_gate_up_packed,
+ *   a_down    [L, E_l, r_dn, I]      -> a_down_packed
+ * (moe_lora_packed_lora_a_bytes bytes each, which = 0 gate_up, 1 down).
+ * Pointers of an inactive projection may be NULL; all others 16-byte
+ * aligned; outputs must not overlap inputs.
+ */
+size_t moe_lora_packed_lora_a_bytes(const moe_lora_shape *shape, int which);
+
+int moe_lora_pack_lora_a(const moe_lora_shape *shape, const void *a_gate_up, const void *a_down,
+                         void *a_gate_up_packed, void *a_down_packed, void *stream);
 
 /*
  * Routing and permutation only.  Routes from `router_logits` (with the

@@ -88,6 +88,10 @@ def load_library(path: str = LIB_PATH):
     lib.moe_lora_packed_w2_bytes.restype = ctypes.c_size_t
     lib.moe_lora_pack_weights.argtypes = [P(Shape), vp, vp, vp, vp, vp]
     lib.moe_lora_pack_weights.restype = ctypes.c_int
+    lib.moe_lora_packed_lora_a_bytes.argtypes = [P(Shape), ctypes.c_int]
+    lib.moe_lora_packed_lora_a_bytes.restype = ctypes.c_size_t
+    lib.moe_lora_pack_lora_a.argtypes = [P(Shape), vp, vp, vp, vp, vp]
+    lib.moe_lora_pack_lora_a.restype = ctypes.c_int
     lib.moe_lora_route_workspace_size.argtypes = [P(Shape)]
     lib.moe_lora_route_workspace_size.restype = ctypes.c_size_t
     lib.moe_lora_route.argtypes = [P(Shape), vp, vp, vp, vp, vp, P(Routing), vp,
@@ -161,6 +165,43 @@ def pack_weights(shape: Shape, w13: torch.Tensor, w2: torch.Tensor):
         ctypes.byref(shape), _ptr(w13, _BF16, (E_l, H, 2 * I), "w13"),
         _ptr(w2, _BF16, (E_l, I, H), "w2"), w13p.data_ptr(), w2p.data_ptr(), _stream()))
     return w13p, w2p
+
+
+def lora_a_shape(shape: Shape, which: int):
+    """Plain shape of a LoRA A stack (which: 0 gate_up, 1 down)."""
+    L, E_l = shape.num_loras, shape.local_num_experts
+    if which == 0:
+        return (L, 1 if shape.lora_shared_outer else E_l, shape.rank_gate_up, shape.hidden)
+    return (L, E_l, shape.rank_down, shape.inter)
+
+
+def packed_lora_a_shape(shape: Shape, which: int):
+    """Shape of a packed LoRA A stack: [L, E_l or 1, ceil(K / 64), r, 64]."""
+    L, outer, r, K = lora_a_shape(shape, which)
+    return (L, outer, (K + 63) // 64, r, 64)
+
+
+def pack_lora_a(shape: Shape, a_gate_up: Optional[torch.Tensor],
+                a_down: Optional[torch.Tensor]):
+    """Packed copies of the LoRA A stacks (bf16, device); None for an inactive
+    projection."""
+    lib = load_library()
+    L = shape.num_loras
+    gu, dn = L > 0 and shape.rank_gate_up > 0, L > 0 and shape.rank_down > 0
+    out = []
+    for which, a, active in ((0, a_gate_up, gu), (1, a_down, dn)):
+        if not active:
+            out.append(None)
+            continue
+        p = torch.empty(packed_lora_a_shape(shape, which), dtype=torch.bfloat16, device=a.device)
+        assert p.numel() * 2 == lib.moe_lora_packed_lora_a_bytes(ctypes.byref(shape), which)
+        out.append(p)
+    gu_src = _ptr(a_gate_up, _BF16, lora_a_shape(shape, 0), "lora_a_gate_up") if gu else None
+    dn_src = _ptr(a_down, _BF16, lora_a_shape(shape, 1), "lora_a_down") if dn else None
+    _check(lib.moe_lora_pack_lora_a(
+        ctypes.byref(shape), gu_src, dn_src, out[0].data_ptr() if gu else None,
+        out[1].data_ptr() if dn else None, _stream()))
+    return out[0], out[1]
 
 
 def alloc_routing(shape: Shape, device) -> Dict[str, torch.Tensor]:
@@ -237,9 +278,11 @@ def _inputs(shape: Shape, hidden, w13_packed, w2_packed, lora_a_gate_up, lora_b_
         _ptr(topk_weights, torch.float32, (T, k), "topk_weights"),
         _ptr(w13_packed, _BF16, (E_l, H, 2 * I), "w13_packed"),
         _ptr(w2_packed, _BF16, (E_l, I, H), "w2_packed"),
-        _ptr(lora_a_gate_up, _BF16, (L, outer, rg, H), "lora_a_gate_up") if gu else None,
+        _ptr(lora_a_gate_up, _BF16, packed_lora_a_shape(shape, 0), "lora_a_gate_up (packed)")
+        if gu else None,
         _ptr(lora_b_gate_up, _BF16, (L, E_l, 2 * I, rg), "lora_b_gate_up") if gu else None,
-        _ptr(lora_a_down, _BF16, (L, E_l, rd, I), "lora_a_down") if dn else None,
+        _ptr(lora_a_down, _BF16, packed_lora_a_shape(shape, 1), "lora_a_down (packed)")
+        if dn else None,
         _ptr(lora_b_down, _BF16, (L, outer, H, rd), "lora_b_down") if dn else None,
         _ptr(token_lora_mapping, torch.int32, (T,), "token_lora_mapping"),
         ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None,
@@ -264,7 +307,9 @@ def forward(shape: Shape, hidden: torch.Tensor, w13_packed: torch.Tensor,
             no_alloc: bool = False) -> Optional[torch.Tensor]:
     """One layer forward on the current stream; returns ``out`` bf16 [T, H].
 
-    With ``expert_out`` (bf16 [T*k, H]) the per-slot expert outputs are
+    ``w13_packed`` / ``w2_packed`` come from :func:`pack_weights` and
+    ``lora_a_gate_up`` / ``lora_a_down`` from :func:`pack_lora_a`; the LoRA B
+    stacks are passed as they are.  With ``expert_out`` (bf16 [T*k, H]) the per-slot expert outputs are
     written there at their permuted rows and the finalize is skipped (returns
     None; needs ``routing``); :func:`finalize` completes it.  ``side_stream``,
     ``fork_event``, ``join_event`` (raw hipStream_t / hipEvent_t handles)
@@ -325,7 +370,8 @@ def finalize(shape: Shape, expert_out: torch.Tensor, routing: Dict[str, torch.Te
 
 
 def layer_from_host(cfg, inputs: Dict, device="cuda"):
-    """Upload host arrays from the input generator and pack the expert weights.
+    """Upload host arrays from the input generator and pack the expert weights
+    and the LoRA A stacks.
 
     Returns a dict of device tensors keyed like the ``forward`` arguments.
     """
@@ -349,10 +395,15 @@ def layer_from_host(cfg, inputs: Dict, device="cuda"):
     }
     if inputs.get("routing_bias") is not None:
         layer["routing_bias"] = torch.from_numpy(inputs["routing_bias"]).to(device)
-    if L > 0 and cfg.rank_gate_up > 0:
-        layer["lora_a_gate_up"] = dev_bf16(inputs["a_gu"])
+    gu, dn = L > 0 and cfg.rank_gate_up > 0, L > 0 and cfg.rank_down > 0
+    a_gu = dev_bf16(inputs["a_gu"]) if gu else None
+    a_dn = dev_bf16(inputs["a_dn"]) if dn else None
+    a_gu_p, a_dn_p = pack_lora_a(shape, a_gu, a_dn)
+    del a_gu, a_dn
+    if gu:
+        layer["lora_a_gate_up"] = a_gu_p
         layer["lora_b_gate_up"] = dev_bf16(inputs["b_gu"])
-    if L > 0 and cfg.rank_down > 0:
-        layer["lora_a_down"] = dev_bf16(inputs["a_dn"])
+    if dn:
+        layer["lora_a_down"] = a_dn_p
         layer["lora_b_down"] = dev_bf16(inputs["b_dn"])
     return shape, layer

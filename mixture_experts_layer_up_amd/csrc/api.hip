@@ -240,6 +240,44 @@ int moe_lora_pack_weights(const moe_lora_shape *shape, const void *w13, const vo
     return check(launch_pack(p2, st));
 }
 
+size_t moe_lora_packed_lora_a_bytes(const moe_lora_shape *shape, int which)
+{
+    if (validate_shape(shape) != MOE_LORA_OK || (which != 0 && which != 1))
+        return 0;
+    const int r = which == 0 ? shape->rank_gate_up : shape->rank_down;
+    if (shape->num_loras <= 0 || r <= 0)
+        return 0;
+    const int K = which == 0 ? shape->hidden : shape->inter;
+    const size_t stacks = (size_t)shape->num_loras *
+                          (which == 0 && shape->lora_shared_outer ? 1 : shape->local_num_experts);
+    return stacks * lora_a_chunks(K) * r * 64 * 2;
+}
+
+int moe_lora_pack_lora_a(const moe_lora_shape *shape, const void *a_gate_up, const void *a_down,
+                         void *a_gate_up_packed, void *a_down_packed, void *stream)
+{
+    MOE_TRY(validate_shape(shape));
+    const bool gu = lora_gate_up_active(shape), dn = lora_down_active(shape);
+    if ((gu && (!a_gate_up || !a_gate_up_packed)) || (dn && (!a_down || !a_down_packed)))
+        return MOE_LORA_ERR_INVALID_ARG;
+    if ((gu && (!aligned(a_gate_up, 16) || !aligned(a_gate_up_packed, 16))) ||
+        (dn && (!aligned(a_down, 16) || !aligned(a_down_packed, 16))))
+        return MOE_LORA_ERR_MISALIGNED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int L = shape->num_loras, E_l = shape->local_num_experts;
+    if (gu) {
+        PackAArgs p{static_cast<const uint16_t *>(a_gate_up), static_cast<uint16_t *>(a_gate_up_packed),
+                    L * (shape->lora_shared_outer ? 1 : E_l), shape->rank_gate_up, shape->hidden};
+        MOE_TRY(check(launch_pack_lora_a(p, st)));
+    }
+    if (dn) {
+        PackAArgs p{static_cast<const uint16_t *>(a_down), static_cast<uint16_t *>(a_down_packed),
+                    L * E_l, shape->rank_down, shape->inter};
+        MOE_TRY(check(launch_pack_lora_a(p, st)));
+    }
+    return MOE_LORA_OK;
+}
+
 size_t moe_lora_route_workspace_size(const moe_lora_shape *shape)
 {
     if (validate_shape(shape) != MOE_LORA_OK)

@@ -84,12 +84,25 @@ struct PackArgs {
     int E_l, K, N, I;      // I > 0: gate/up interleaved tile order (w13)
 };
 
+// The packed LoRA A layout the shrink kernels read.  Per stack (one r x K
+// matrix), K runs in chunks of 64 values (the last one zero-padded), and a
+// chunk holds the r rank rows' 64 values one after another:
+//   element (stack, q, k) at ((stack * lora_a_chunks(K) + k / 64) * r + q) * 64 + k % 64
+// so that the rank rows of one chunk are one contiguous r x 128-byte run.
+__host__ __device__ inline int lora_a_chunks(int K) { return (K + 63) >> 6; }
+
+struct PackAArgs {
+    const uint16_t *src;   // [stacks, r, K], row-major
+    uint16_t *dst;         // [stacks, lora_a_chunks(K), r, 64]
+    int stacks, r, K;      // K % 32 == 0
+};
+
 // LoRA shrink S[p] = A[l, e] * X(row), grouped by (adapter, local expert).
 struct ShrinkArgs {
     const uint16_t *X;        // gather_by_token ? hidden [T, K] : act [n, K]
     int gather_by_token;
     int K;
-    const uint16_t *A;        // [L, E_l, r, K]
+    const uint16_t *A;        // packed [L, E_l (shared: 1), lora_a_chunks(K), r, 64]
     int r, rp, L, E_l, k;
     const int32_t *seg_offsets, *seg_slots, *exp2perm;
     uint16_t *S;              // [n, rp], row = slot x = t * k + j
@@ -146,6 +159,7 @@ struct FinalizeArgs {
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
 hipError_t launch_permute(const PermuteArgs &a, hipStream_t s);
 hipError_t launch_pack(const PackArgs &a, hipStream_t s);
+hipError_t launch_pack_lora_a(const PackAArgs &a, hipStream_t s);
 hipError_t launch_shrink(const ShrinkArgs &a, hipStream_t s);
 // launch_shrink's choices: the many-row kernel, else the few-row kernel with
 // 16 * shrink_row_tiles(a) rows per pass

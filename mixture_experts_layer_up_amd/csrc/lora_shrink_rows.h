@@ -3,10 +3,11 @@
 // S[x, 0:rp] = A[l, e] x_row for the slots x of one virtual expert (adapter
 // l, local expert e), 16 * MT rows per pass; q >= r is written as 0.  S is
 // indexed by slot, so the gate_up shrink (rows = the slots' tokens) needs no
-// permutation lookup at all.  The stack A[l, e] (r x K) is K-contiguous per
-// rank row, which is exactly the per-lane B operand layout of the MFMA (8
-// consecutive K values of one column q).  NS 16-column tiles of q per pass
-// over N; the block's 4 waves split K.  Sources: "BF16 support for the
+// permutation lookup at all.  The stack A[l, e] (r x K, packed in 64-value K
+// chunks, kernels.h) is K-contiguous per rank row inside a chunk, which is
+// exactly the per-lane B operand layout of the MFMA (8 consecutive K values
+// of one column q).  NS 16-column tiles of q per pass over N; the block's 4
+// waves split K.  Sources: "BF16 support for the
 // experimental_sgl_trtllm MoE-LoRA path", Flow section 2 (shrink then expand
 // per virtual expert), and the "PR #28091 report", key source snippets (the
 // shrink intermediate has one rank-r row per (token, top-k choice)).
@@ -37,16 +38,19 @@ __device__ __forceinline__ void shrink_rows(const ShrinkArgs &a, int stack, int 
     const int kbeg = min(KC, wave * kc_per);
     const int nm = min(KC, kbeg + kc_per) - kbeg;
     const int n_nt = (a.r + 15) >> 4;
-    const uint16_t *abase = a.A + (size_t)stack * a.r * a.K + (lane >> 4) * 8;
+    // the packed stack: 64-value K chunks, each holding the r rank rows
+    const uint16_t *abase =
+        a.A + (size_t)stack * lora_a_chunks(a.K) * a.r * 64 + (lane >> 4) * 8;
 
     Stage<MT, NS, CH> s0, s1;
     auto load_b_nt = [&](int nt0, int vc, u32x4 (&b)[NS]) {
-        const int kc = kbeg + vc;
+        const int kc = kbeg + vc;  // 32-value chunk: half kc % 2 of packed chunk kc / 2
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
             const int q = (nt0 + n) * 16 + (lane & 15);
             // q >= r reads a clamped valid row; those output columns are not stored
-            b[n] = load16_stream(abase + (size_t)min(q, a.r - 1) * a.K + kc * 32);
+            b[n] = load16_stream(abase + ((size_t)(kc >> 1) * a.r + min(q, a.r - 1)) * 64 +
+                                 (kc & 1) * 32);
         }
     };
     // the stack's first stage does not depend on the rows: issue it before

@@ -51,7 +51,43 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a)
     store16(a.dst + f * 8, v);
 }
 
+// One-time relayout of LoRA A stacks (the shrink's operand) into 64-value K
+// chunks that hold all rank rows of the chunk contiguously (kernels.h,
+// lora_a_chunks).  The shrink kernels read a stack chunk by chunk, every rank
+// row at once; row-major stacks spread each chunk over r rows 2K bytes
+// apart.  One thread per 16-byte output piece; K % 32 == 0, so a piece lies
+// wholly inside K or wholly in the zero padding.
+__global__ __launch_bounds__(256) void pack_lora_a_kernel(PackAArgs a)
+{
+    const size_t f = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const int C = lora_a_chunks(a.K);
+    const size_t total = (size_t)a.stacks * C * a.r * 8;
+    if (f >= total)
+        return;
+    const int u = (int)(f & 7);  // 16-byte piece inside the 64-value row chunk
+    size_t rest = f >> 3;
+    const int q = (int)(rest % a.r);
+    rest /= a.r;
+    const int c = (int)(rest % C);
+    const size_t stack = rest / C;
+    const int k0 = c * 64 + u * 8;
+    u32x4 v{0u, 0u, 0u, 0u};
+    if (k0 < a.K)
+        v = load16(a.src + (stack * a.r + q) * a.K + k0);
+    store16(a.dst + f * 8, v);
+}
+
 } // namespace
+
+hipError_t launch_pack_lora_a(const PackAArgs &a, hipStream_t s)
+{
+    const size_t total = (size_t)a.stacks * lora_a_chunks(a.K) * a.r * 8;
+    if (total == 0)
+        return hipSuccess;
+    const size_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(pack_lora_a_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_pack(const PackArgs &a, hipStream_t s)
 {

@@ -167,6 +167,40 @@ def test_route_and_pack_validation(lib):
     assert lib.moe_lora_packed_w2_bytes(ctypes.byref(shape)) == 8 * 64 * 128 * 2
 
 
+@pytest.mark.parametrize("cfg,gu,dn", [
+    # tiny: H 128, I 64, L 2, E_l 8, ranks 4: stacks of 2 and 1 chunks
+    (CONFIGS["tiny"], 2 * 8 * 2 * 4 * 64 * 2, 2 * 8 * 1 * 4 * 64 * 2),
+    # I 96: the down stacks' 2 chunks hold 32 values of padding
+    (CONFIGS["tiny"].replace(inter=96, rank_gate_up=12, rank_down=8),
+     2 * 8 * 2 * 12 * 64 * 2, 2 * 8 * 2 * 8 * 64 * 2),
+    # shared-outer: one gate_up stack per adapter
+    (CONFIGS["decode64"].replace(lora_shared_outer=True), 4 * 1 * 32 * 16 * 64 * 2,
+     4 * 128 * 12 * 16 * 64 * 2),
+    # rank 0 on down: no packed down stack
+    (CONFIGS["tiny"].replace(rank_down=0), 2 * 8 * 2 * 4 * 64 * 2, 0)])
+def test_packed_lora_a_bytes(lib, cfg, gu, dn):
+    shape = binding.make_shape(cfg)
+    assert lib.moe_lora_packed_lora_a_bytes(ctypes.byref(shape), 0) == gu
+    assert lib.moe_lora_packed_lora_a_bytes(ctypes.byref(shape), 1) == dn
+    assert lib.moe_lora_packed_lora_a_bytes(ctypes.byref(shape), 2) == 0
+    assert lib.moe_lora_packed_lora_a_bytes(None, 0) == 0
+
+
+def test_pack_lora_a_validation(lib):
+    shape = binding.make_shape(CONFIGS["tiny"])
+    f = _fake
+    assert lib.moe_lora_pack_lora_a(ctypes.byref(shape), None, f(), f(), f(), None) == ERR_INVALID_ARG
+    assert lib.moe_lora_pack_lora_a(ctypes.byref(shape), f(), f(), f(), None, None) == ERR_INVALID_ARG
+    assert lib.moe_lora_pack_lora_a(ctypes.byref(shape), f(4096 + 2), f(), f(), f(),
+                                    None) == ERR_ALIGN
+    assert lib.moe_lora_pack_lora_a(ctypes.byref(shape), f(), f(), f(), f(4096 + 8),
+                                    None) == ERR_ALIGN
+    assert lib.moe_lora_pack_lora_a(None, f(), f(), f(), f(), None) == ERR_INVALID_ARG
+    # no adapters: nothing to pack, every pointer may be NULL
+    none = binding.make_shape(CONFIGS["tiny"].replace(num_loras=0))
+    assert lib.moe_lora_pack_lora_a(ctypes.byref(none), None, None, None, None, None) == 0
+
+
 def _routing_fake():
     return binding.Routing(*[_fake(8192 * (i + 1)) for i in range(len(binding.Routing._fields_))])
 

@@ -1,4 +1,5 @@
-"""The one-time weight pack against the layout its header documents.
+"""The one-time packs (expert weights, LoRA A stacks) against the layouts
+the header documents.
 
 moe_lora_pack_weights writes, for expert e, 64-column slab s, K chunk c,
 16-column tile t, lane l and element i, the bf16 at
@@ -8,6 +9,10 @@ W[e][32 c + 8 (l // 16) + i][col(4 s + t) + l % 16], with col(n) = (n % 2) * I
 w2.  The expected arrays below are that formula written with numpy index
 arrays; the weights are random 16-bit patterns, so any value the pack moved
 to the wrong place, or changed, shows.
+
+moe_lora_pack_lora_a writes the bf16 A[s][q][k] of stack s (r x K) at
+((s * C + k // 64) * r + q) * 64 + k % 64, C = ceil(K / 64), with zeros for
+the padding past K; checked the same way.
 """
 import numpy as np
 import pytest
@@ -50,3 +55,39 @@ def test_pack_matches_documented_layout(E, H, I):
     # the inputs are left as they were
     np.testing.assert_array_equal(d13.view(torch.int16).cpu().numpy(), w13)
     np.testing.assert_array_equal(d2.view(torch.int16).cpu().numpy(), w2)
+
+
+def lora_a_packed_by_formula(a):
+    """The documented packed order of LoRA A stacks a [L, O, r, K]: per stack,
+    ceil(K / 64) chunks of the r rank rows' 64 values, zeros past K."""
+    L, O, r, K = a.shape
+    C = (K + 63) // 64
+    padded = np.zeros((L, O, r, C * 64), a.dtype)
+    padded[..., :K] = a
+    l, o, c, q, u = np.meshgrid(np.arange(L), np.arange(O), np.arange(C), np.arange(r),
+                                np.arange(64), indexing="ij")
+    return padded[l, o, q, 64 * c + u].reshape(-1)
+
+
+@pytest.mark.parametrize("H,I,L,E,rg,rd,shared", [
+    (256, 96, 3, 4, 24, 12, False),   # I % 64 == 32: the down stack's last chunk is half padding
+    (128, 64, 2, 3, 4, 20, False),    # ranks that are not multiples of 8
+    (192, 160, 2, 5, 16, 16, True),   # shared-outer gate_up stacks: one per adapter
+    (2048, 768, 4, 8, 64, 64, False)])
+def test_lora_a_pack_matches_documented_layout(H, I, L, E, rg, rd, shared):
+    announce(f"pack lora A H={H} I={I} L={L} E={E} r={rg}/{rd} shared={shared}")
+    cfg = LayerConfig("pack_a", 1, H, I, E, 1, 0, E, L, rg, rd, seed=0, lora_shared_outer=shared)
+    shape = binding.make_shape(cfg)
+    rng = np.random.default_rng(70 + H + L)
+    a_gu = rng.integers(-2 ** 15, 2 ** 15, size=(L, 1 if shared else E, rg, H), dtype=np.int16)
+    a_dn = rng.integers(-2 ** 15, 2 ** 15, size=(L, E, rd, I), dtype=np.int16)
+    d_gu = torch.from_numpy(a_gu).cuda().view(torch.bfloat16)
+    d_dn = torch.from_numpy(a_dn).cuda().view(torch.bfloat16)
+    p_gu, p_dn = binding.pack_lora_a(shape, d_gu, d_dn)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(p_gu.view(torch.int16).cpu().numpy().reshape(-1),
+                                  lora_a_packed_by_formula(a_gu))
+    np.testing.assert_array_equal(p_dn.view(torch.int16).cpu().numpy().reshape(-1),
+                                  lora_a_packed_by_formula(a_dn))
+    np.testing.assert_array_equal(d_gu.view(torch.int16).cpu().numpy(), a_gu)
+    np.testing.assert_array_equal(d_dn.view(torch.int16).cpu().numpy(), a_dn)

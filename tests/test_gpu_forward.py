@@ -134,6 +134,20 @@ def test_prefill_all_rows():
         assert np.abs(got[a * 512:(a + 1) * 512]).max() > 0.1 * np.abs(ref).max()
 
 
+def test_prefill_bitwise_run_to_run():
+    """The many-row path has no atomics and no order-dependent sums: two
+    forwards of the prefill layer agree bit for bit."""
+    announce("forward prefill run-to-run")
+    cfg = CONFIGS["prefill"]
+    inp = cached_inputs("prefill")
+    layer = binding.layer_from_host(cfg, inp)
+    a, ra = run_forward(cfg, inp, routing=True, layer=layer)
+    b, rb = run_forward(cfg, inp, routing=True, layer=layer)
+    np.testing.assert_array_equal(a, b)
+    for name in ra:
+        np.testing.assert_array_equal(ra[name], rb[name], err_msg=name)
+
+
 def test_prefill_4096_tokens_all_rows():
     """A 4096-token prefill (32,768 slots): 207 .. 303 rows per expert, so two
     176-row tiles per expert in the many-row GEMMs (the second ragged), more
